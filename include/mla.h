@@ -1,0 +1,147 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) paged MLA decode library (libmla.so).
+ *
+ * Operation.  Decode attention for Multi-head Latent Attention over a paged
+ * latent KV cache.  Every query head attends to one shared latent key row per
+ * token: the first 512 dims are the compressed latent c_t, the last 64 the rope
+ * key.  Scores use the absorbed query q~ = [W_UK^T q_nope ; q_rope] against the
+ * whole 576-wide row (the absorption identity q.(W_UK c) = (W_UK^T q).c of the
+ * "FlashMLA inference acceleration" notes, dpshk.com/news/5996785, §2.1), and
+ * the output is the softmax-weighted sum of the latent part (the first dv = 512
+ * dims); the caller applies W_UV afterwards.  Softmax runs over the whole
+ * cached sequence and equals the textbook result (same notes, §2.2, online
+ * softmax).  The two calls mirror the FlashMLA API -- one metadata call from the
+ * sequence lengths, then the paged decode with 64-token pages addressed through
+ * block_table and cache_seqlens, query heads folded onto their KV head
+ * ("OpenSourceWeek Day 1 -- Demystifying DeepSeek's FlashMLA",
+ * deepseekonline.chat, §II.1, §II.2, §V.2).
+ *
+ * For batch b, query token s < s_q, query head h, KV head k = h / (h_q / h_kv),
+ * L = cache_seqlens[b]:
+ *   N        = L, or max(0, L - s_q + s + 1) when causal (the s_q queries are
+ *              the newest s_q cached tokens, so query s sees keys t <= L-s_q+s)
+ *   K_t      = kcache[block_table[b][t / 64], t % 64, k, 0:576],  t < N
+ *   x_t      = softmax_scale * (q[b,s,h,:] . K_t)
+ *   out      = sum_t softmax(x)_t * K_t[0:512]          (bf16, round-to-nearest-even)
+ *   lse      = ln(sum_t exp(x_t))                       (fp32, natural log)
+ *   N == 0   => out = 0, lse = -inf
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers; every buffer is caller-owned; the
+ *     library allocates no device memory and keeps no state between calls.
+ *   - Calls are asynchronous: they validate their arguments on the host, enqueue
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream) and return.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Return value: MLA_OK or a negative status; mla_last_error() then gives a
+ *     message (thread-local).  Argument checks run before any HIP call, so an
+ *     invalid call touches no device state.
+ *   - Data-dependent validity (cache_seqlens <= max_blocks * 64, page ids
+ *     referenced by the first ceil(L/64) block_table entries in [0, num_pages))
+ *     is the caller's contract.  The kernels never read outside the cache: an
+ *     out-of-range page id is read as a page of zeros.
+ *   - Layouts are dense row-major: q [batch, s_q, h_q, 576] bf16,
+ *     kcache [num_pages, 64, h_kv, 576] bf16, block_table [batch, max_blocks]
+ *     int32, cache_seqlens [batch] int32, out [batch, s_q, h_q, 512] bf16,
+ *     lse [batch, s_q, h_q] fp32.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID (-1)     /* null pointer, non-positive size, h_q % h_kv != 0, num_parts mismatch */
+#define MLA_ERR_UNSUPPORTED (-2) /* d_qk != 576, dv != 512, page size != 64, batch above MLA_MAX_BATCH */
+#define MLA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than mla_plan's size */
+#define MLA_ERR_HIP (-4)         /* a HIP runtime call failed; see mla_last_error() */
+
+#define MLA_PAGE_BLOCK_SIZE 64
+#define MLA_D_QK 576
+#define MLA_DV 512
+#define MLA_METADATA_INTS 8  /* ints per tile_metadata row */
+#define MLA_MAX_BATCH 8192   /* sequences per call (metadata kernel keeps prefix sums on chip) */
+
+/*
+ * mla_plan -- host only, launches nothing.
+ * Chooses the number of parts P the split-KV scheduler cuts the work into and
+ * the workspace size mla_decode_paged needs.
+ *   batch        number of sequences (1..MLA_MAX_BATCH)
+ *   rows_per_kv  s_q * h_q / h_kv: query rows that share one KV head
+ *                (the fold of the Day-1 page §II.1 and the second argument of
+ *                get_mla_metadata in §V.2)
+ *   h_kv         KV heads (>= 1)
+ *   dv           value width, must be 512
+ *   num_cus      compute units to plan for; 0 = query the current device
+ *   num_parts    out: P (>= 1)
+ *   workspace_bytes out: bytes of device workspace for mla_decode_paged
+ *                (batch + P) * h_kv * rows_per_kv * (dv + 1) * 4
+ * Errors: MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP (device query).
+ */
+int mla_plan(int batch, int rows_per_kv, int h_kv, int dv, int num_cus,
+             int* num_parts, size_t* workspace_bytes);
+
+/*
+ * mla_tile_rows -- host only.  Query rows one workgroup owns for a given
+ * rows_per_kv (16 or 64); the decode grid has ceil(rows/tile) row tiles.
+ */
+int mla_tile_rows(int rows_per_kv);
+
+/*
+ * mla_get_metadata -- split-KV schedule for one decode step (the
+ * get_mla_metadata call of the Day-1 page §V.2; the variable-length balancing
+ * the "Flash MLA: efficient MLA decoding kernel library for variable-length
+ * sequences" page, developer.baidu.com, motivates in §二).
+ * One kernel on `stream` reads cache_seqlens and writes
+ *   tile_metadata [num_parts, 8] int32: per part
+ *       {first_seq, first_block, last_seq, end_block_of_last_seq, first_chunk_ordinal, 0, 0, 0}
+ *       (an empty part is {batch, 0, batch, 0, 0, 0, 0, 0});
+ *   num_splits [batch + 1] int32: exclusive prefix sum of chunks per sequence.
+ * Work is counted in 64-token pages, each sequence costing max(ceil(L/64), 1)
+ * pages plus a fixed per-chunk overhead; parts get equal shares.  The result
+ * depends only on (cache_seqlens, rows_per_kv, num_parts) and is reused by
+ * every layer of the step.  h_kv only enters through num_parts.
+ * Errors: MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_HIP (launch).
+ */
+int mla_get_metadata(const int32_t* cache_seqlens, int batch, int rows_per_kv, int h_kv,
+                     int num_parts, int32_t* tile_metadata, int32_t* num_splits, void* stream);
+
+/*
+ * mla_decode_paged -- the decode (flash_mla_with_kvcache of the Day-1 page §V.2).
+ * Enqueues the split-KV decode kernel and, when any sequence is split into
+ * more than one chunk, the log-sum-exp combine kernel.
+ *   q             bf16 bits [batch, s_q, h_q, d_qk]
+ *   kcache        bf16 bits [num_pages, page_block_size, h_kv, d_qk]
+ *   num_pages     pages in kcache (used to keep reads inside the cache)
+ *   block_table   int32 [batch, max_blocks]; entries past ceil(L/64) are ignored
+ *   cache_seqlens int32 [batch], each >= 0
+ *   d_qk, dv, page_block_size   must be 576, 512, 64
+ *   tile_metadata, num_splits   from mla_get_metadata with the same
+ *                 cache_seqlens, rows_per_kv = s_q*h_q/h_kv and num_parts
+ *   causal        0/1 (bottom-right aligned when s_q > 1)
+ *   softmax_scale scale applied to q.k (e.g. 1/sqrt(192))
+ *   out           bf16 bits [batch, s_q, h_q, dv]
+ *   lse           fp32 [batch, s_q, h_q], natural log
+ *   workspace     device scratch of at least mla_plan's workspace_bytes, holding
+ *                 fp32 partial outputs and their lse for split sequences
+ * Errors: MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_HIP.
+ */
+int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages,
+                     const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                     int batch, int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                     const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                     int causal, float softmax_scale, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* mla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

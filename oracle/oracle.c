@@ -183,17 +183,11 @@ int oracle_decode(const uint16_t* q, const uint16_t* kcache, long long num_pages
  * j the last sequence whose work starts before hi, last = min(hi, B_j) - 1;
  * an empty part (lo >= T) is {b, 0, b, 0, 0, 0, 0, 0}.
  *
- * Tile rows and the constants: rows <= 16 -> 16, <= 32 -> 32, <= 64 -> 64,
- * else 128 (the row tile one workgroup owns); OVH = max(1, tile / 16);
- * QMIN = 2 * OVH.
+ * Tile rows and the constants: rows <= 16 -> 16, else 64 (the row tile one
+ * workgroup owns); OVH = max(1, tile / 16); QMIN = 2 * OVH.
  * Written with plain loops over all sequences for every part.
  */
-static int twin_tile_rows(int rows) {
-  if (rows <= 16) return 16;
-  if (rows <= 32) return 32;
-  if (rows <= 64) return 64;
-  return 128;
-}
+static int twin_tile_rows(int rows) { return rows <= 16 ? 16 : 64; }
 
 int oracle_tile_rows(int rows) { return twin_tile_rows(rows); }
 

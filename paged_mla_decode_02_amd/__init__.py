@@ -1,0 +1,168 @@
+"""Paged MLA decode for AMD MI355X (gfx950).
+
+Thin Python binding over libmla.so (see include/mla.h).  Every step of the
+decode runs in the library's HIP kernels; this module only marshals torch
+tensors (device memory and the current stream) into the C ABI.  Importing it
+fails loudly when the library has not been built.
+
+Low-level calls, same names as the C ABI:
+    mla_plan, mla_tile_rows, mla_get_metadata, mla_decode_paged
+The two-call FlashMLA-style API ("OpenSourceWeek Day 1 -- Demystifying
+DeepSeek's FlashMLA", deepseekonline.chat, §V.2):
+    get_mla_metadata(cache_seqlens, s_q * h_q // h_kv, h_kv) -> (tile_metadata, num_splits)
+    flash_mla_with_kvcache(q, k_cache, block_table, cache_seqlens, dv,
+                           tile_metadata, num_splits, causal=False,
+                           softmax_scale=None) -> (out, lse)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "MlaError", "mla_plan", "mla_tile_rows", "mla_get_metadata", "mla_decode_paged",
+    "get_mla_metadata", "flash_mla_with_kvcache",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+PAGE_BLOCK_SIZE = 64
+D_QK = 576
+DV = 512
+
+
+class MlaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libmla error {code}: {msg}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m paged_mla_decode_02_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.mla_plan.argtypes = [I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(SZ)]
+    lib.mla_plan.restype = I
+    lib.mla_tile_rows.argtypes = [I]
+    lib.mla_tile_rows.restype = I
+    lib.mla_get_metadata.argtypes = [P, I, I, I, I, P, P, P]
+    lib.mla_get_metadata.restype = I
+    lib.mla_decode_paged.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
+                                     ctypes.c_float, P, P, P, SZ, P]
+    lib.mla_decode_paged.restype = I
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise MlaError(rc, _lib.mla_last_error().decode(errors="replace"))
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mla_tile_rows(rows_per_kv: int) -> int:
+    r = _lib.mla_tile_rows(int(rows_per_kv))
+    _check(min(r, 0))
+    return r
+
+
+def mla_plan(batch: int, rows_per_kv: int, h_kv: int, dv: int = DV, num_cus: int = 0) -> Tuple[int, int]:
+    """(num_parts, workspace_bytes) for a decode step."""
+    parts = ctypes.c_int(0)
+    ws = ctypes.c_size_t(0)
+    _check(_lib.mla_plan(int(batch), int(rows_per_kv), int(h_kv), int(dv), int(num_cus),
+                         ctypes.byref(parts), ctypes.byref(ws)))
+    return parts.value, ws.value
+
+
+def mla_get_metadata(cache_seqlens: torch.Tensor, rows_per_kv: int, h_kv: int,
+                     num_parts: Optional[int] = None, num_cus: int = 0):
+    """Split-KV schedule: (tile_metadata int32 [P, 8], num_splits int32 [b + 1])."""
+    _require(cache_seqlens, "cache_seqlens", torch.int32)
+    b = cache_seqlens.numel()
+    if num_parts is None:
+        num_parts, _ = mla_plan(b, rows_per_kv, h_kv, DV, num_cus)
+    dev = cache_seqlens.device
+    md = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+    ns = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    _check(_lib.mla_get_metadata(cache_seqlens.data_ptr(), b, int(rows_per_kv), int(h_kv),
+                                 int(num_parts), md.data_ptr(), ns.data_ptr(), _stream(dev)))
+    return md, ns
+
+
+def mla_decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                     cache_seqlens: torch.Tensor, dv: int, tile_metadata: torch.Tensor,
+                     num_splits: torch.Tensor, causal: bool, softmax_scale: float,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Paged decode; returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q])."""
+    _require(q, "q", torch.bfloat16)
+    _require(kcache, "kcache", torch.bfloat16)
+    _require(block_table, "block_table", torch.int32)
+    _require(cache_seqlens, "cache_seqlens", torch.int32)
+    _require(tile_metadata, "tile_metadata", torch.int32)
+    _require(num_splits, "num_splits", torch.int32)
+    if q.dim() != 4 or kcache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [b, s_q, h_q, d], kcache [pages, 64, h_kv, d], block_table [b, n]")
+    b, s_q, h_q, d_qk = q.shape
+    num_pages, page, h_kv, d_k = kcache.shape
+    if d_k != d_qk:
+        raise ValueError("q and kcache must have the same head dim")
+    if h_kv <= 0 or h_q % h_kv:
+        raise ValueError("h_q must be a multiple of h_kv")
+    num_parts = tile_metadata.shape[0]
+    rows = s_q * h_q // h_kv
+    dev = q.device
+    if out is None:
+        out = torch.empty((b, s_q, h_q, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.bfloat16)
+    _require(lse, "lse", torch.float32)
+    need = (b + num_parts) * h_kv * rows * (dv + 1) * 4
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(_lib.mla_decode_paged(
+        q.data_ptr(), kcache.data_ptr(), num_pages, block_table.data_ptr(), block_table.shape[1],
+        cache_seqlens.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
+        num_parts, num_splits.data_ptr(), int(bool(causal)), float(softmax_scale),
+        out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(dev)))
+    return out, lse
+
+
+def get_mla_metadata(cache_seqlens: torch.Tensor, num_heads_per_head_k: int, num_heads_k: int):
+    """FlashMLA-style metadata call: (tile_metadata, num_splits)."""
+    return mla_get_metadata(cache_seqlens, num_heads_per_head_k, num_heads_k)
+
+
+def flash_mla_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                           cache_seqlens: torch.Tensor, head_dim_v: int, tile_metadata: torch.Tensor,
+                           num_splits: torch.Tensor, softmax_scale: Optional[float] = None,
+                           causal: bool = False):
+    """FlashMLA-style decode: (out, lse).  softmax_scale defaults to d_qk ** -0.5."""
+    if softmax_scale is None:
+        softmax_scale = q.shape[-1] ** -0.5
+    return mla_decode_paged(q, k_cache, block_table, cache_seqlens, head_dim_v, tile_metadata,
+                            num_splits, causal, softmax_scale)

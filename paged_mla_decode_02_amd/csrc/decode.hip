@@ -1,0 +1,683 @@
+// Paged MLA decode for gfx950 (CDNA4): split-KV attention of absorbed queries
+// over one shared latent KV head stored in 64-token pages.
+//
+// Method.  For each query row, softmax(scale * q.K^T) . V over the cached
+// sequence, where K is the whole 576-wide latent+rope row and V its first 512
+// dims (the absorbed form of MLA: q.(W_UK c) = (W_UK^T q).c, "FlashMLA inference
+// acceleration" notes, dpshk.com/news/5996785, §2.1).  The softmax is computed
+// online, block by block, with a running max and sum; earlier blocks are
+// rescaled when the max grows, which gives exactly the textbook softmax (same
+// notes, §2.2).  All query heads that share the KV head are folded into the
+// rows of one problem (Day-1 page "OpenSourceWeek Day 1 -- Demystifying
+// DeepSeek's FlashMLA", deepseekonline.chat, §II.1), so every latent page read
+// from HBM is multiplied against all of them: a dense contraction per page.
+//
+// gfx950 design (the pages' Hopper kernel -- cp.async into shared memory and
+// warpgroup MMA, Day-1 page §II.3 -- is prior art only):
+//   * pages move HBM -> LDS with buffer_load ... lds (16 bytes per lane, no
+//     register staging); out-of-range slots of the last page read as zeros
+//     through the buffer descriptor's size, so stale cache bits never reach V;
+//   * a page lives in LDS as four 16-token slices; a slice is laid out
+//     [9 groups of 8 chunks][16 tokens][8 chunks of 16 B] with the chunk index
+//     XOR-swizzled inside its 128-byte group, so that the K-operand reads (16
+//     tokens x 16 B per quarter wave) and the transposed V-operand reads
+//     (ds_read_b64_tr_b16, 4 tokens x 64 B per half wave) are bank-conflict free,
+//     and every read or DMA address is one of a few per-lane bases plus an
+//     immediate offset;
+//   * QK^T and PV run on v_mfma_f32_32x32x16_bf16 (16x16 shapes for <= 16
+//     rows), accumulating in fp32; P is rounded to bf16 for PV and the row sum
+//     uses the fp32 P;
+//   * the running max is only moved when it grows by more than 2^8 (in log2
+//     units), so the O rescale is rare; the final normalisation uses the same
+//     reference max, which keeps the result exact up to rounding.
+//
+// Two kernels:
+//   decode_tokensplit  (<= 16 query rows per KV head, memory-bound shapes):
+//     each of the 4 waves owns 16 tokens of every page and an independent online
+//     softmax over them; the 4 states merge at the end of a chunk through LDS.
+//   decode_pairsplit  (64-row tiles, compute-bound shapes):
+//     QK^T is split 2 x 2 over rows and tokens (32 rows per wave, queries
+//     resident in registers), P goes through LDS, and PV is split by output dims
+//     (128 per wave), so each V element of a page is read from LDS once per
+//     workgroup.
+#include <utility>
+
+#include "mla_kernels.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4_t rsrc, LDS_AS void* lds, int size,
+                                                           int voffset, int soffset, int offset,
+                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+constexpr int kThreads = 256;
+constexpr int kSlice = 16;                         // tokens one wave moves per page
+constexpr int kSliceBytes = kSlice * kRowBytes;    // 18432 = 18 x 1 KB DMA instructions
+constexpr int kSliceDma = kSliceBytes / 1024;
+constexpr int kGroupBytes = 16 * 128;              // 8 chunks x 16 tokens
+constexpr int kPageBytes = kPage * kRowBytes;      // 73728
+constexpr float kTau = 8.0f;                       // lazy-rescale threshold, log2 units
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// XOR applied to a chunk's position inside its 8-chunk group, by token (0..15).
+// Over the 8 even (or 8 odd) tokens of a slice it is a permutation of 0..7, and
+// tokens 4u and 4u+2 (4u+1 and 4u+3) differ in bit 2.
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+// byte offset of (token t in 0..15, chunk c in 0..71) inside a 16-token slice
+__device__ __forceinline__ int slice_off(int t, int c) {
+  return (c >> 3) * kGroupBytes + t * 128 + (((c & 7) ^ swz(t)) << 4);
+}
+
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const unsigned long long a = (unsigned long long)base;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Explicit waits: the LDS-DMA loads are tracked by hand, never by a compiler fence.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ float wave_max16(float v) {  // max over lanes l, l^16, l^32, l^48
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+// reduction across the two wave halves (lane l and l ^ 32)
+__device__ __forceinline__ float half_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
+}
+
+__device__ __forceinline__ bf16x4_t lds_tr16(const LDS_AS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)p);
+}
+
+// Which part / row tile / KV head this workgroup serves.  With xcd_map the
+// workgroups of one part (its row tiles and KV heads, which read the same pages)
+// get ids that differ by multiples of 8, i.e. land on the same XCD and share L2.
+__device__ __forceinline__ void map_block(const DecodeParams& p, int& part, int& mt, int& kvh) {
+  const int x = blockIdx.x;
+  const int G = p.m_tiles * p.h_kv;
+  int g;
+  if (p.xcd_map) {
+    const int k = x >> 3;
+    g = k % G;
+    part = (k / G) * 8 + (x & 7);
+  } else {
+    part = x / G;
+    g = x % G;
+  }
+  mt = g % p.m_tiles;
+  kvh = g / p.m_tiles;
+}
+
+struct SeqRange {
+  int L, nb, lo, hi, ord, chunks;
+  bool ok;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b, int i0, int f0, int j0,
+                                              int e0, int ord0) {
+  SeqRange r;
+  r.L = p.seqlens[b];
+  if (r.L < 0) r.L = 0;
+  r.nb = (r.L + kPage - 1) / kPage;
+  r.lo = (b == i0) ? f0 : 0;
+  r.hi = (b == j0) ? e0 : (r.nb > 1 ? r.nb : 1);
+  if (r.hi > r.nb) r.hi = r.nb;
+  if (r.lo < 0) r.lo = 0;
+  if (r.lo > r.hi) r.lo = r.hi;
+  r.ord = (b == i0) ? ord0 : 0;
+  r.chunks = p.num_splits[b + 1] - p.num_splits[b];
+  // metadata that does not belong to these lengths / part count must not make
+  // the epilogue write outside the workspace: such a chunk writes nothing
+  const long long slot = (long long)p.num_splits[b] + r.ord;
+  r.ok = r.ord >= 0 && r.ord < r.chunks && slot >= 0 && slot < (long long)p.batch + p.num_parts;
+  return r;
+}
+
+// Resource descriptor for page `blk` of sequence b: the page's bytes for this
+// layout, clipped to the valid tokens so slots past L (and unknown page ids)
+// read as zeros.
+__device__ __forceinline__ i32x4_t page_rsrc(const DecodeParams& p, int b, int blk, int L) {
+  const int pid = blk < p.max_blocks
+                      ? __builtin_amdgcn_readfirstlane(p.block_table[(long long)b * p.max_blocks + blk])
+                      : -1;
+  int valid = L - blk * kPage;
+  if (valid > kPage) valid = kPage;
+  const bool ok = pid >= 0 && (long long)pid < p.num_pages;
+  const long long page_stride = (long long)kPage * p.h_kv * kRowBytes;
+  const char* base = (const char*)p.kcache + (ok ? (long long)pid * page_stride : 0);
+  return make_rsrc(base, ok ? (uint32_t)(valid * p.h_kv * kRowBytes) : 0u);
+}
+
+// Per-lane source offsets of a slice DMA: instruction (half th, group g) writes
+// LDS bytes [g*2048 + th*1024, +1024) = tokens 8th..8th+7 of chunk group g, and
+// lane i supplies token 8th + i/8, chunk 8g + ((i%8) ^ swz(token)).  The byte
+// offset is vbase[th] + 128*g, so two registers cover all 18 instructions.
+struct SliceDma {
+  int vbase[2];
+};
+__device__ __forceinline__ SliceDma slice_dma_offsets(int tok0, int kvh, int h_kv, int lane) {
+  SliceDma d;
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    const int t = 8 * th + (lane >> 3);
+    d.vbase[th] = ((tok0 + t) * h_kv + kvh) * kRowBytes + (((lane & 7) ^ swz(t)) << 4);
+  }
+  return d;
+}
+// The instruction's immediate offset would move the LDS destination as well, so
+// the group's source offset goes into the per-lane offset instead.
+template <int G>
+__device__ __forceinline__ void dma_group(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d) {
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (LDS_AS void*)(dst + G * kGroupBytes), 16, d.vbase[0] + G * 128,
+                                  0, 0, 0);
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (LDS_AS void*)(dst + G * kGroupBytes + 1024), 16,
+                                  d.vbase[1] + G * 128, 0, 0, 0);
+}
+template <int... Gs>
+__device__ __forceinline__ void dma_groups(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d,
+                                           std::integer_sequence<int, Gs...>) {
+  (dma_group<Gs>(dst, rsrc, d), ...);
+}
+// Move tokens [tok0, tok0 + 16) of one page (KV head kvh) into a 16-token LDS
+// slice: 18 instructions (9 chunk groups x 2 token halves).
+__device__ __forceinline__ void dma_slice(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d) {
+  dma_groups(dst, rsrc, d, std::make_integer_sequence<int, 9>{});
+}
+
+__device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh, int row, int& s,
+                                           long long& qo) {
+  s = row / p.group;
+  const int h = kvh * p.group + row % p.group;
+  qo = ((long long)b * p.s_q + s) * p.h_q + h;  // flat (b, s, h) index
+}
+
+// ---------------------------------------------------------------------------
+// <= 16 rows: token-split kernel.
+// LDS: per wave two 16-token slices (2 x 18432 B) + merge statistics.
+constexpr int kTsLds = 4 * 2 * kSliceBytes + 4 * 16 * 2 * 4;
+
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+decode_tokensplit(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
+  LDS_AS char* smem = (LDS_AS char*)smem_generic;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int part, mt, kvh;
+  map_block(p, part, mt, kvh);
+  const int32_t* md = p.tile_md + (long long)part * kMdInts;
+  const int i0 = md[0], f0 = md[1], e0 = md[3], ord0 = md[4];
+  const int j0 = min(md[2], p.batch - 1);
+  if (i0 >= p.batch || i0 < 0) return;
+
+  LDS_AS char* slices = smem + w * 2 * kSliceBytes;
+  LDS_AS float* mstat = (LDS_AS float*)(smem + 4 * 2 * kSliceBytes);  // [4 waves][16 rows][2]
+
+  // lane roles: QK output / PV operand B -> query row (lane & 15)
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+  const int row = mt * 16 + r16;
+  const bool row_ok = row < p.rows;
+  // per-lane LDS bases inside a slice (see slice_off)
+  int kaddr[2], vaddr[4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) kaddr[k] = slice_off(r16, 4 * k + grp);
+  {
+    const int tt = grp * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) vaddr[k] = slice_off(tt, 2 * k + ((lane & 3) >> 1)) + ((lane & 1) << 3);
+  }
+
+  for (int b = i0; b <= j0; ++b) {
+    const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
+    int s;
+    long long qo;
+    row_coords(p, b, kvh, row_ok ? row : 0, s, qo);
+    const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
+
+    // queries: B operand of the 16x16x32 QK MFMA, 8 dims per lane per k-step
+    bf16x8_t qreg[18];
+    {
+      const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk) + grp;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        bf16x8_t v = qp[ks * 4];
+        qreg[ks] = row_ok ? v : bf16x8_t{};
+      }
+    }
+    f32x4_t O[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+    if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, b, sr.lo, sr.L), dma);
+    for (int blk = sr.lo; blk < sr.hi; ++blk) {
+      const int st = (blk - sr.lo) & 1;
+      if (blk + 1 < sr.hi) {
+        dma_slice(slices + (st ^ 1) * kSliceBytes, page_rsrc(p, b, blk + 1, sr.L), dma);
+        wait_vmcnt<kSliceDma>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      const LDS_AS char* reg = slices + st * kSliceBytes;
+
+      // S^T[16 tokens x 16 rows] = K_slice . Q^T ; A-operand row = token r16,
+      // chunk 4*ks + grp = group ks/2, position 4*(ks&1) + grp
+      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        const bf16x8_t a = *(const LDS_AS bf16x8_t*)(reg + kaddr[ks & 1] + (ks >> 1) * kGroupBytes);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], S, 0, 0, 0);
+      }
+      // online softmax over this wave's 16 tokens: lane holds tokens grp*4 + i of row r16
+      const int tok0 = blk * kPage + w * kSlice + grp * 4;
+      float x[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (tok0 + i < nkeys) ? S[i] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      }
+      mx = wave_max16(mx);
+      float alpha = 1.f;
+      if (mx > m_run + kTau) {
+        alpha = __builtin_amdgcn_exp2f(m_run - mx);  // 0 when m_run == -inf
+        m_run = mx;
+        l_run *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float pr[4];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+        ps += pr[i];
+      }
+      l_run += wave_sum16(ps);
+      u32x2_t pb = {pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])};
+      const s16x4_t pbs = __builtin_bit_cast(s16x4_t, pb);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) O[i] *= alpha;
+      }
+      // O^T[16 dims x 16 rows] += V^T[16 dims x 16 tokens] . P^T, 32 dim tiles;
+      // dims 16*dt + (lane&3)*4 = group dt/4, position 2*(dt&3) + (lane&3)/2
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) {
+        const bf16x4_t a = lds_tr16(reg + vaddr[dt & 3] + (dt >> 2) * kGroupBytes);
+        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), pbs,
+                                                          O[dt], 0, 0, 0);
+      }
+    }
+
+    // ---- merge the four waves' partial softmax states (LDS), then write
+    wg_barrier();  // every wave is done with its slices
+    if (lane < 16) {
+      mstat[(w * 16 + lane) * 2 + 0] = m_run;
+      mstat[(w * 16 + lane) * 2 + 1] = l_run;
+    }
+    wg_barrier();
+    {
+      float M = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) M = fmaxf(M, mstat[(v * 16 + r16) * 2]);
+      const float c_own = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) O[i] *= c_own;
+    }
+    // reducer lane mapping: row lane >> 2, 16 dims at (lane & 3) * 16 within a 64-dim slab
+    const int rr = lane >> 2;
+    const int rrow = mt * 16 + rr;
+    float M = -INFINITY, lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, mstat[(v * 16 + rr) * 2]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float mv = mstat[(v * 16 + rr) * 2];
+      lsum += (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M) * mstat[(v * 16 + rr) * 2 + 1];
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    int rs;
+    long long ro;
+    row_coords(p, b, kvh, rrow < p.rows ? rrow : 0, rs, ro);
+    const bool split = sr.chunks > 1;
+    const long long slot_row =
+        (((long long)(p.num_splits[b] + sr.ord) * p.h_kv + kvh) * p.rows + rrow);
+    constexpr int kDumpStride = 260;  // floats per row: 256 + 4 pad
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      LDS_AS float* dump = (LDS_AS float*)slices;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+        *(LDS_AS f32x4_t*)(dump + r16 * kDumpStride + dt * 16 + grp * 4) = O[half * 16 + dt];
+      wg_barrier();
+      f32x4_t acc[4] = {};
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const LDS_AS float* src = (const LDS_AS float*)(smem + v * 2 * kSliceBytes);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          acc[k] += *(const LDS_AS f32x4_t*)(src + rr * kDumpStride + w * 64 + (lane & 3) * 16 + k * 4);
+      }
+      if (rrow < p.rows && sr.ok) {
+        const int d0 = half * 256 + w * 64 + (lane & 3) * 16;
+        if (split) {
+          f32x4_t* dst = (f32x4_t*)(p.o_acc + slot_row * kDv + d0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) dst[k] = acc[k] * inv;
+        } else {
+          u32x4_t pk[2];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f32x4_t v = acc[k] * inv;
+            pk[k >> 1][(k & 1) * 2 + 0] = pack_bf16(v[0], v[1]);
+            pk[k >> 1][(k & 1) * 2 + 1] = pack_bf16(v[2], v[3]);
+          }
+          u32x4_t* dst = (u32x4_t*)(p.out + ro * kDv + d0);
+          dst[0] = pk[0];
+          dst[1] = pk[1];
+        }
+      }
+      wg_barrier();
+    }
+    if (w == 0 && (lane & 3) == 0 && rrow < p.rows && sr.ok) {
+      const float l2 = lsum > 0.f ? M + __builtin_amdgcn_logf(lsum) : -INFINITY;
+      if (split) p.lse_acc[slot_row] = l2;
+      else p.lse[ro] = l2 * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 64-row tiles: pair-split kernel.
+// The 4 waves form a 2 x 2 grid: wave w owns query rows 32*(w&1) .. +31 (its
+// queries stay in registers) and tokens 32*(w>>1) .. +31 of every page for
+// QK^T.  The two waves of a row group agree on one running max per page through
+// LDS, so their P blocks share a reference; P goes to LDS and PV is split by
+// output dims (128 per wave, all 64 rows), which reads every V element of the
+// page from LDS once per workgroup.
+// LDS: two page buffers, P [64 rows x 64 tokens] bf16, the per-page row maxima
+// of both token groups, alpha, and the end-of-chunk (m, l) of both token groups.
+constexpr int kPsRows = 64;
+constexpr int kPsPbuf = 2 * kPageBytes;
+constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
+constexpr int kPsAbuf = kPsXmax + 2 * kPsRows * 4;
+constexpr int kPsSbuf = kPsAbuf + kPsRows * 4;
+constexpr int kPsLds = kPsSbuf + 2 * kPsRows * 2 * 4;
+
+// P row r holds 64 bf16 tokens as 8 chunks of 16 bytes; chunk c is stored at
+// position c ^ ((r >> 1) & 7), which keeps 16 consecutive rows reading the same
+// chunk on 16 different bank groups.
+__device__ __forceinline__ int pbuf_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+decode_pairsplit(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
+  LDS_AS char* smem = (LDS_AS char*)smem_generic;
+  LDS_AS char* pages = smem;
+  LDS_AS char* pbuf = smem + kPsPbuf;
+  LDS_AS float* xmax = (LDS_AS float*)(smem + kPsXmax);  // [2 token groups][64 rows]
+  LDS_AS float* abuf = (LDS_AS float*)(smem + kPsAbuf);  // [64 rows]
+  LDS_AS float* sbuf = (LDS_AS float*)(smem + kPsSbuf);  // [2 token groups][64 rows][2]
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int part, mt, kvh;
+  map_block(p, part, mt, kvh);
+  const int32_t* md = p.tile_md + (long long)part * kMdInts;
+  const int i0 = md[0], f0 = md[1], e0 = md[3], ord0 = md[4];
+  const int j0 = min(md[2], p.batch - 1);
+  if (i0 >= p.batch || i0 < 0) return;
+
+  const int l32 = lane & 31;
+  const int hb = lane >> 5;   // which 8-element half of a k-step this lane holds
+  const int g16 = lane >> 4;
+  const int k16 = lane & 15;
+  const int rg = w & 1;       // row group of this wave in QK
+  const int tg = w >> 1;      // token group of this wave in QK
+  const int trow = rg * 32 + l32;          // row inside the tile (QK phase)
+  const int qrow = mt * kPsRows + trow;
+  const bool qrow_ok = qrow < p.rows;
+
+  // K operand of QK: token 32*tg + l32 -> slice 2*tg + l32/16, token l32 & 15;
+  // chunk 2*ks + hb -> group ks/4, position 2*(ks&3) + hb.
+  int kaddr[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) kaddr[k] = (2 * tg + (l32 >> 4)) * kSliceBytes + slice_off(l32 & 15, 2 * k + hb);
+  // V^T operand of PV (transposed read) for tokens 16*ks + 8*(g16>>1) + k16/4 (+4):
+  // slice ks, token 8*(g16>>1) + k16/4 (+4); dims 128*w + 32*dt + 16*(g16&1) + 4*(k16&3)
+  // -> group 2*w + dt/2, position 4*(dt&1) + 2*(g16&1) + (k16&3)/2, byte 8*(k16&1).
+  int vaddr[2][2];
+#pragma unroll
+  for (int p4 = 0; p4 < 2; ++p4)
+#pragma unroll
+    for (int d1 = 0; d1 < 2; ++d1) {
+      const int t = 8 * (g16 >> 1) + (k16 >> 2) + 4 * p4;
+      const int pos = 4 * d1 + 2 * (g16 & 1) + ((k16 & 3) >> 1);
+      vaddr[p4][d1] = t * 128 + ((pos ^ swz(t)) << 4) + ((k16 & 1) << 3) + 2 * w * kGroupBytes;
+    }
+  // P^T operand of PV: row 32*rt + l32, tokens 16*ks + 8*hb .. +7 = chunk 2*ks + hb
+  int paddr[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) paddr[rt][ks] = pbuf_off(rt * 32 + l32, 2 * ks + hb);
+  const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+
+  for (int b = i0; b <= j0; ++b) {
+    const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
+    int s;
+    long long qo;
+    row_coords(p, b, kvh, qrow_ok ? qrow : 0, s, qo);
+    const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
+
+    bf16x8_t qreg[36];
+    {
+      const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk) + hb;
+#pragma unroll
+      for (int ks = 0; ks < 36; ++ks) {
+        bf16x8_t v = qp[ks * 2];
+        qreg[ks] = qrow_ok ? v : bf16x8_t{};
+      }
+    }
+    f32x16_t O[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) O[dt][0] = O[dt][1] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.f;  // l_run covers this wave's token group only
+
+    if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, b, sr.lo, sr.L), dma);
+    for (int blk = sr.lo; blk < sr.hi; ++blk) {
+      const int pb = (blk - sr.lo) & 1;
+      wait_vmcnt<0>();
+      wg_barrier();  // page blk visible; the other buffer, P and xmax are free
+      if (blk + 1 < sr.hi)
+        dma_slice(pages + (pb ^ 1) * kPageBytes + w * kSliceBytes, page_rsrc(p, b, blk + 1, sr.L), dma);
+      const LDS_AS char* page = pages + pb * kPageBytes;
+
+      // ---- S^T[32 tokens x 32 rows] = K . Q^T, two accumulation chains,
+      // K operands fetched three k-steps ahead
+      f32x16_t S;
+      {
+        f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
+        bf16x8_t ka[4];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          ka[i] = *(const LDS_AS bf16x8_t*)(page + kaddr[i & 3] + (i >> 2) * kGroupBytes);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+          if (ks + 3 < 36) {
+            const int n = ks + 3;
+            ka[n & 3] = *(const LDS_AS bf16x8_t*)(page + kaddr[n & 3] + (n >> 2) * kGroupBytes);
+          }
+          if (ks & 1) S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3], qreg[ks], S1, 0, 0, 0);
+          else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3], qreg[ks], S0, 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        S = S0 + S1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page
+      const int tok0 = blk * kPage + 32 * tg + 4 * hb;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = tok0 + 8 * (r >> 2) + (r & 3);
+        S[r] = (tok < nkeys) ? S[r] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, S[r]);
+      }
+      mx = half_max(mx);
+      if (hb == 0) xmax[tg * kPsRows + trow] = mx;
+      wg_barrier();  // both token groups' maxima visible
+      mx = fmaxf(mx, xmax[(tg ^ 1) * kPsRows + trow]);
+      float alpha = 1.f;
+      if (mx > m_run + kTau) {  // identical decision in both waves of the row group
+        alpha = __builtin_amdgcn_exp2f(m_run - mx);
+        m_run = mx;
+        l_run *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S[r] = __builtin_amdgcn_exp2f(S[r] - m_use);
+        ps += S[r];
+      }
+      l_run += half_sum(ps);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2_t v = {pack_bf16(S[4 * j], S[4 * j + 1]), pack_bf16(S[4 * j + 2], S[4 * j + 3])};
+        *(LDS_AS u32x2_t*)(pbuf + pbuf_off(trow, 4 * tg + j) + hb * 8) = v;
+      }
+      if (tg == 0 && hb == 0) abuf[trow] = alpha;
+      __builtin_amdgcn_sched_barrier(0);
+      wg_barrier();  // P and alpha visible
+
+      // ---- O^T[128 dims x 64 rows] += V^T . P^T over the page's 64 tokens
+      {
+        const float a0 = abuf[l32], a1 = abuf[32 + l32];
+        if (__builtin_amdgcn_ballot_w64(a0 != 1.f || a1 != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            O[dt][0] *= a0;
+            O[dt][1] *= a1;
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8_t bp0 = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
+        const bf16x8_t bp1 = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
+        const LDS_AS char* vs = page + ks * kSliceBytes;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int go = (dt >> 1) * kGroupBytes;
+          const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
+          const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
+          const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp0, O[dt][0], 0, 0, 0);
+          O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp1, O[dt][1], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- epilogue: (m, l) of both token groups for every row
+    if (hb == 0) {
+      sbuf[(tg * kPsRows + trow) * 2 + 0] = m_run;
+      sbuf[(tg * kPsRows + trow) * 2 + 1] = l_run;
+    }
+    wg_barrier();
+    const bool split = sr.chunks > 1;
+    const long long slot = (long long)(p.num_splits[b] + sr.ord) * p.h_kv + kvh;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int rl = rt * 32 + l32;
+      const int orow = mt * kPsRows + rl;
+      const float mrow = sbuf[rl * 2 + 0];  // same reference in both token groups
+      const float lrow = sbuf[rl * 2 + 1] + sbuf[(kPsRows + rl) * 2 + 1];
+      const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+      if (orow < p.rows && sr.ok) {
+        int os;
+        long long oo;
+        row_coords(p, b, kvh, orow, os, oo);
+        const long long srow = slot * p.rows + orow;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d0 = w * 128 + dt * 32 + 8 * j + 4 * hb;
+            f32x4_t v = {O[dt][rt][4 * j], O[dt][rt][4 * j + 1], O[dt][rt][4 * j + 2], O[dt][rt][4 * j + 3]};
+            v *= inv;
+            if (split) {
+              *(f32x4_t*)(p.o_acc + srow * kDv + d0) = v;
+            } else {
+              u32x2_t pk = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+              *(u32x2_t*)(p.out + oo * kDv + d0) = pk;
+            }
+          }
+        }
+        if (w == 0 && hb == 0) {
+          const float l2 = lrow > 0.f ? mrow + __builtin_amdgcn_logf(lrow) : -INFINITY;
+          if (split) p.lse_acc[srow] = l2;
+          else p.lse[oo] = l2 * kLn2;
+        }
+      }
+    }
+    wg_barrier();  // sbuf and page buffers are reused by the next sequence
+  }
+}
+
+template <typename K>
+hipError_t launch_one(K kernel, int lds, const DecodeParams& p, hipStream_t stream) {
+  // allow the kernel more than the default 64 KB of dynamic LDS (once per process)
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const int grid = p.num_parts * p.m_tiles * p.h_kv;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (tile_rows_for(p.rows) == 16) return launch_one(decode_tokensplit, kTsLds, p, stream);
+  return launch_one(decode_pairsplit, kPsLds, p, stream);
+}
+
+}  // namespace mla

@@ -1,0 +1,46 @@
+// Internal interface between the host API (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPage = 64;          // tokens per cache page
+constexpr int kDqk = 576;          // latent 512 + rope 64
+constexpr int kDv = 512;           // value width (latent part of each row)
+constexpr int kRowBytes = kDqk * 2;
+constexpr int kMdInts = 8;
+constexpr int kMaxBatch = 8192;
+
+// Query rows one workgroup owns: <= 16 rows use the 16-row token-split kernel,
+// larger row counts the 64-row pair-split kernel (ceil(rows / 64) row tiles).
+__host__ __device__ constexpr int tile_rows_for(int rows) { return rows <= 16 ? 16 : 64; }
+// Fixed per-chunk cost, in page units, that the scheduler charges before each
+// sequence: loading the query tile and writing / re-reading a split partial.
+__host__ __device__ constexpr int sched_overhead(int tile) { return tile / 16 > 1 ? tile / 16 : 1; }
+__host__ __device__ constexpr int sched_min_part(int tile) { return 2 * sched_overhead(tile); }
+
+struct DecodeParams {
+  const uint16_t* q;         // [b, s_q, h_q, 576]
+  const uint16_t* kcache;    // [num_pages, 64, h_kv, 576]
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const int32_t* tile_md;    // [num_parts, 8]
+  const int32_t* num_splits; // [b + 1]
+  uint16_t* out;             // [b, s_q, h_q, 512]
+  float* lse;                // [b, s_q, h_q]
+  float* o_acc;              // [slots, h_kv, rows, 512]
+  float* lse_acc;            // [slots, h_kv, rows]
+  int64_t num_pages;
+  int batch, s_q, h_q, h_kv, rows, group, max_blocks, num_parts, m_tiles, causal;
+  float scale_log2;          // softmax_scale * log2(e)
+  int xcd_map;               // workgroup -> (part, row tile, kv head) mapping keeps a part on one XCD
+};
+
+hipError_t launch_metadata(const int32_t* seqlens, int batch, int rows, int num_parts,
+                           int32_t* tile_md, int32_t* num_splits, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace mla

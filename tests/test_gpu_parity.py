@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: out relative L2 <= 1e-2, lse absolute <= 1e-3 (rows the oracle gives -inf
+must be -inf), tile metadata and num_splits bit-exact against the oracle twin.
+Small workloads compare every element; the full-size workloads compare a seeded
+sample of query rows (the oracle computes them one by one) plus properties that
+hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    import paged_mla_decode_02_amd as mla
+    oracle.build(force=False)
+    return torch, mla, oracle.default(), torch.device("cuda:0")
+
+
+def upload(torch, w, dev):
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kc = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.cache_seqlens).to(dev)
+    return q, kc, bt, sl
+
+
+def run(env, w, num_parts=None, tensors=None):
+    torch, mla, _, dev = env
+    q, kc, bt, sl = tensors if tensors is not None else upload(torch, w, dev)
+    md, ns = mla.mla_get_metadata(sl, w.rows, w.h_kv, num_parts=num_parts)
+    out, lse = mla.mla_decode_paged(q, kc, bt, sl, w.dv, md, ns, w.causal, w.scale)
+    torch.cuda.synchronize()
+    return md.cpu().numpy(), ns.cpu().numpy(), out, lse
+
+
+def as_np(out, lse):
+    o = out.float().cpu().numpy().astype(np.float64)
+    return o.reshape(-1, o.shape[-1]), lse.cpu().numpy().astype(np.float64).reshape(-1)
+
+
+def check(out, lse, ref_out, ref_lse, sel=None, what=""):
+    go, gl = as_np(out, lse)
+    if sel is not None:
+        go, gl = go[sel], gl[sel]
+    assert np.all(np.isfinite(go)), f"{what}: non-finite output"
+    ninf = np.isneginf(ref_lse)
+    assert np.array_equal(np.isneginf(gl), ninf), f"{what}: -inf lse rows differ"
+    assert np.all(go[ninf] == 0), f"{what}: rows without keys must be zero"
+    denom = np.linalg.norm(ref_out)
+    rel = np.linalg.norm(go - ref_out) / denom if denom > 0 else np.linalg.norm(go)
+    err = np.max(np.abs(gl[~ninf] - ref_lse[~ninf])) if np.any(~ninf) else 0.0
+    assert rel <= OUT_TOL, f"{what}: out rel L2 {rel:.3e} > {OUT_TOL}"
+    assert err <= LSE_TOL, f"{what}: lse abs err {err:.3e} > {LSE_TOL}"
+    return rel, err
+
+
+def sample_queries(w, n, seed):
+    rng = np.random.default_rng(seed)
+    total = w.batch * w.s_q * w.h_q
+    sel = set(rng.choice(total, size=min(n, total), replace=False).tolist())
+    sel |= {0, total - 1}
+    per_b = w.s_q * w.h_q
+    for b in range(w.batch):  # at least one row of every sequence
+        sel.add(b * per_b + int(rng.integers(per_b)))
+    return np.array(sorted(sel), dtype=np.int64)
+
+
+# ------------------------------------------------------------------ metadata
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_metadata_bit_exact_configs(env, cfg):
+    torch, mla, orc, dev = env
+    w = workloads.config_workload(cfg)
+    sl = torch.from_numpy(w.cache_seqlens).to(dev)
+    md, ns = mla.mla_get_metadata(sl, w.rows, w.h_kv)
+    md_ref, ns_ref = orc.schedule(w.cache_seqlens, w.rows, md.shape[0])
+    assert np.array_equal(md.cpu().numpy(), md_ref)
+    assert np.array_equal(ns.cpu().numpy(), ns_ref)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_metadata_bit_exact_random(env, seed):
+    torch, mla, orc, dev = env
+    rng = np.random.default_rng(100 + seed)
+    b = int(rng.integers(1, 3000))
+    lens = rng.integers(0, int(rng.choice([2, 65, 5000, 100000])), size=b).astype(np.int32)
+    rows = int(rng.choice([1, 16, 17, 64, 128, 256]))
+    P = int(rng.choice([1, 7, 64, 256, 1500]))
+    md, ns = mla.mla_get_metadata(torch.from_numpy(lens).to(dev), rows, 1, num_parts=P)
+    md_ref, ns_ref = orc.schedule(lens, rows, P)
+    assert np.array_equal(md.cpu().numpy(), md_ref)
+    assert np.array_equal(ns.cpu().numpy(), ns_ref)
+
+
+# ------------------------------------------------------------------ the five workloads
+def test_config0_tiny_full(env):
+    w = workloads.config_workload(0)
+    md, ns, out, lse = run(env, w)
+    ref = env[2].decode(w)
+    check(out, lse, *ref, what="tiny")
+
+
+def test_config1_memory_bound_full(env):
+    w = workloads.config_workload(1)
+    md, ns, out, lse = run(env, w)
+    ref = env[2].decode(w)
+    check(out, lse, *ref, what="memory-bound")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_large_configs_sampled(env, cfg):
+    torch = env[0]
+    w = workloads.config_workload(cfg)
+    md, ns, out, lse = run(env, w)
+    sel = sample_queries(w, 160, seed=cfg)
+    ref_out, ref_lse = env[2].decode(w, sel=sel)
+    check(out, lse, ref_out, ref_lse, sel=sel, what=f"config {cfg}")
+    # properties of every row: finite, bounded by the largest |V| element, lse finite
+    go, gl = as_np(out, lse)
+    assert np.all(np.isfinite(gl))
+    vmax = float(np.max(np.abs(workloads.bf16_to_f32(w.kcache[..., :512]))))
+    assert np.max(np.abs(go)) <= vmax * (1 + 1e-2)
+    del torch
+
+
+# ------------------------------------------------------------------ edge cases
+EDGE = [
+    # lens, s_q, h_q, h_kv, causal, num_parts
+    ([1], 1, 16, 1, False, None),
+    ([63, 64, 65, 1, 0, 128], 1, 16, 1, False, None),
+    ([0, 0], 1, 16, 1, False, None),
+    ([0, 0], 2, 64, 1, True, None),
+    ([65, 129, 1, 2, 3], 2, 16, 1, True, None),        # L % 64 == 1 with causal s_q = 2
+    ([65, 129, 1, 2, 3], 2, 64, 1, True, 3),
+    ([1000, 1, 70], 1, 8, 1, False, 2),
+    ([1000, 1, 70], 1, 16, 2, False, None),            # two KV heads, 8 q heads each
+    ([300, 77], 2, 32, 2, True, 5),
+    ([4096, 100], 1, 128, 1, False, 7),
+    ([513, 2049, 64], 2, 128, 1, True, 16),
+    ([700, 900], 1, 17, 1, False, 9),                  # 17 rows: one ragged 64-row tile
+    ([700, 900], 3, 32, 1, True, 11),                  # 96 rows: two tiles, second ragged
+    ([5000], 1, 64, 1, False, 64),                     # many splits of one sequence
+    ([5000], 1, 16, 1, False, 64),
+    ([2, 3000, 1, 640], 1, 1, 1, False, None),         # a single query row
+]
+
+
+@pytest.mark.parametrize("lens,s_q,h_q,h_kv,causal,P", EDGE)
+def test_edge_cases(env, lens, s_q, h_q, h_kv, causal, P):
+    w = make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal, seed=sum(lens) + s_q,
+                      extra_pages=2, poison_tail=True, outliers=True)
+    md, ns, out, lse = run(env, w, num_parts=P)
+    md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
+    assert np.array_equal(md, md_ref) and np.array_equal(ns, ns_ref)
+    ref = env[2].decode(w)
+    check(out, lse, *ref, what=f"edge {lens} s_q={s_q} h_q={h_q} h_kv={h_kv} P={P}")
+
+
+def test_large_scores_rescale(env):
+    """Scores far apart (|x| up to ~300 in log2 units) force the lazy rescale path."""
+    w = make_workload([3000, 640, 129], s_q=2, h_q=64, causal=True, seed=21)
+    ramp = np.linspace(0, 40, 3000 * 0 + w.num_pages * 64).astype(np.float32)
+    kc = workloads.bf16_to_f32(w.kcache).reshape(w.num_pages * 64, -1)
+    kc = kc * ramp[:, None]
+    w.kcache = workloads.bf16_bits(kc).reshape(w.kcache.shape)
+    md, ns, out, lse = run(env, w, num_parts=6)
+    ref = env[2].decode(w)
+    check(out, lse, *ref, what="rescale")
+
+
+# ------------------------------------------------------------------ determinism / invariance
+def test_determinism_bitwise(env):
+    torch = env[0]
+    w = workloads.config_workload(1)
+    t = upload(torch, w, env[3])
+    _, _, o1, l1 = run(env, w, tensors=t)
+    _, _, o2, l2 = run(env, w, tensors=t)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("cfg,rows_h", [(0, None), (None, 64)])
+def test_page_permutation_bitwise(env, cfg, rows_h):
+    torch = env[0]
+    if cfg is not None:
+        w = workloads.config_workload(cfg)
+    else:
+        w = make_workload([1000, 77, 4000], s_q=1, h_q=rows_h, seed=3)
+    _, _, o1, l1 = run(env, w)
+    wp = workloads.permute_pages(w, 9)
+    _, _, o2, l2 = run(env, wp)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_out_of_range_page_ids_are_safe(env):
+    """An out-of-range page id reads as zeros instead of faulting."""
+    torch = env[0]
+    w = make_workload([200, 100], s_q=1, h_q=16, seed=4)
+    w.block_table[0, 1] = w.num_pages + 1000
+    _, _, out, lse = run(env, w)
+    go, gl = as_np(out, lse)
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    del torch
