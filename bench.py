@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Paged MLA decode benchmark on one MI355X.
+
+One step = one pass of the whole decode hot path over one batch: the split-KV
+schedule (mla_get_metadata), the decode kernel (mla_decode_splitkv) and the
+log-sum-exp combine (mla_combine_splits), with q and the paged cache already
+resident in HBM.  Steps are replayed from HIP graphs (one per cache copy).  The
+cache is rotated over enough copies that the working set exceeds the 256 MB
+MALL, so reads come from HBM.
+
+Prints ONE JSON line:
+  value          algorithmic bytes per step / wall time per step (TB/s)
+  roofline       the decode kernel's achieved bandwidth (or MFMA rate) against
+                 MI355X's published peak, from per-launch HIP events
+  cpu_baseline   the fp64 CPU oracle on the host cores (a reported baseline)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {0..4}]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+MALL_BYTES = 256 << 20
+
+
+def algorithmic(w):
+    """Bytes and flops the method must move / compute for one step.
+
+    bytes: every valid latent+rope row once (V is reused from the same bytes),
+    the queries in, out + lse out, block-table entries and lengths.
+    flops: 2 * keys * (576 + 512) per query row (scores and P.V)."""
+    import numpy as np
+    L = w.cache_seqlens.astype(np.int64)
+    nb = (L + 63) // 64
+    kv = int(L.sum()) * w.h_kv * 576 * 2
+    qio = w.batch * w.s_q * w.h_q * (576 * 2 + 512 * 2 + 4)
+    meta = int(nb.sum()) * 4 + w.batch * 4
+    if w.causal:
+        keys = sum(int(max(0, Li - w.s_q + s + 1)) for Li in L for s in range(w.s_q)) * w.h_q
+    else:
+        keys = int(L.sum()) * w.s_q * w.h_q
+    flops = 2 * keys * (576 + 512)
+    return kv + qio + meta, flops, kv
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "mla_kernels.h"):
+        with open(os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, launch_kind):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    or None when missing or taken on a different version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "decode_counters.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload)
+    if not rec or rec.get("kernel_digest") != source_digest() or rec.get("launch") != launch_kind:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, bytes_step, target_s):
+    """The oracle as it stands, on the host cores, over the whole workload
+    repeated until about target_s seconds of CPU work have run."""
+    import oracle
+    orc = oracle.default()
+    cores = len(os.sched_getaffinity(0))
+    orc.set_threads(cores)
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.decode(w)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or runs >= 1000:
+            break
+    per_run = el / runs
+    return {"value": round(bytes_step / per_run / 1e12, 6), "unit": "TB/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"the whole workload ({w.batch} sequences, {w.batch * w.s_q * w.h_q} query rows), "
+                      f"fp64, repeated {runs}x over {el:.1f} s; {per_run * 1e3:.1f} ms per pass"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default: memory-bound)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(collectives and sharding are out of scope); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_mla_decode_02_amd as mla
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = workloads.CONFIGS[args.config]
+    w = workloads.config_workload(args.config)
+    bytes_step, flops_step, kv_bytes = algorithmic(w)
+
+    # inputs resident in HBM; enough cache copies to defeat the MALL
+    kc_bytes = w.kcache.nbytes
+    ncopies = max(1, math.ceil(2 * MALL_BYTES / kc_bytes))
+    kc_host = torch.from_numpy(w.kcache.view(np.int16))
+    kcs = [kc_host.to(dev).view(torch.bfloat16) for _ in range(ncopies)]
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.cache_seqlens).to(dev)
+    P, ws_bytes = mla.mla_plan(w.batch, w.rows, w.h_kv)
+    md = torch.empty((P, 8), dtype=torch.int32, device=dev)
+    ns = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+
+    def step(c, evs=None):
+        if evs is not None:
+            evs[0].record()
+        mla.mla_get_metadata(sl, w.rows, w.h_kv, num_parts=P, out=(md, ns))
+        if evs is not None:
+            evs[1].record()
+        mla.mla_decode_splitkv(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
+        if evs is not None:
+            evs[2].record()
+        mla.mla_combine_splits(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
+        if evs is not None:
+            evs[3].record()
+
+    K, W = args.steps, args.warmup
+    for i in range(3):
+        step(i % ncopies)  # eager warm-up (kernel attributes, allocator)
+    torch.cuda.synchronize()
+
+    mode = "eager"
+    replay = warm = None
+    if not args.eager:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            graphs = []
+            with torch.cuda.stream(s):
+                for c in range(ncopies):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        step(c)
+                    graphs.append(g)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            replay = graphs
+            mode = "hip_graph"
+        except Exception as e:  # graphs unavailable: fall back to eager launches
+            print(f"graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            replay = None
+
+    def run_step(i):
+        if replay is not None:
+            replay[i % ncopies].replay()
+        else:
+            step(i % ncopies)
+
+    # warm-up steps (untimed)
+    for i in range(W):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, each a graph replay of schedule + decode + combine
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        run_step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+
+    # per-kernel durations: HIP events around every launch on the launch stream,
+    # enqueued behind a GPU busy-wait so that the host is always ahead of the GPU
+    # and the events bracket back-to-back kernels rather than launch gaps
+    n_ev = min(K, 100)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(40e6))  # ~20 ms of spinning at ~2 GHz
+    for i in range(n_ev):
+        step(i % ncopies, events[i])
+    torch.cuda.synchronize()
+    durs = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(3)] for i in range(n_ev)])
+    meta_ms, dec_ms, comb_ms = durs.mean(axis=0)
+    dec_p = np.percentile(durs[:, 1], [10, 50, 90])
+
+    tbps = bytes_step / (ms_per_step * 1e-3) / 1e12
+    intensity = flops_step / bytes_step
+    bound = "hbm" if intensity < RIDGE else "mfma"
+    dec_gbs = bytes_step / (dec_ms * 1e-3) / 1e9
+    dec_tflops = flops_step / (dec_ms * 1e-3) / 1e12
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dec_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)}
+    traffic = traffic_from_profiles(cfg["name"], "decode")
+    roof["traffic"] = traffic
+    roof["kernel"] = "decode (mla_decode_splitkv)"
+    roof["launch_ms"] = round(float(dec_ms), 5)
+
+    line = {
+        "metric": "paged MLA decode bf16: achieved TB/s & TFLOPS, % of MI355X roofline",
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg["name"], "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
+            "d_qk": 576, "dv": 512, "page_block_size": 64, "causal": w.causal,
+            "seqlens": {"kind": cfg["lens"][0], "params": list(cfg["lens"][1:]), "seed": w.seed,
+                        "total_tokens": int(w.cache_seqlens.sum())},
+            "softmax_scale": w.scale, "num_parts": P, "cache_copies": ncopies, "launch": mode,
+        },
+        "tflops": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline_frac_step": round(max(bytes_step / (HBM_PEAK_GBS * 1e9), flops_step / (BF16_PEAK_TFLOPS * 1e12))
+                                    / (ms_per_step * 1e-3), 4),
+        "algorithmic": {"bytes_per_step": int(bytes_step), "flops_per_step": int(flops_step),
+                        "flop_per_byte": round(intensity, 2)},
+        "kernel_ms": {"metadata": round(float(meta_ms), 5), "decode": round(float(dec_ms), 5),
+                      "combine": round(float(comb_ms), 5),
+                      "decode_p10_p50_p90": [round(float(x), 5) for x in dec_p], "launches": n_ev},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, bytes_step, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

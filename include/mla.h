@@ -137,6 +137,28 @@ int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages,
                      int causal, float softmax_scale, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The two stages of mla_decode_paged as separate calls, same arguments and
+ * errors.  mla_decode_splitkv enqueues the decode kernel only: sequences kept
+ * in one chunk get out/lse, split sequences leave fp32 partials in `workspace`.
+ * mla_combine_splits then merges those partials into out/lse (the log-sum-exp
+ * combine of the split chunks, the reduction the num_splits output of the
+ * Day-1 page §V.2 implies).  Issued in this order on one stream they equal
+ * mla_decode_paged; apart they let a caller time or overlap the stages.
+ */
+int mla_decode_splitkv(const void* q, const void* kcache, int64_t num_pages,
+                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                       int batch, int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                       const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                       int causal, float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages,
+                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                       int batch, int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                       const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                       int causal, float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-zero status returned on this thread ("" if none). */
 const char* mla_last_error(void);
 

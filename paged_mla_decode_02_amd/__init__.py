@@ -6,7 +6,8 @@ tensors (device memory and the current stream) into the C ABI.  Importing it
 fails loudly when the library has not been built.
 
 Low-level calls, same names as the C ABI:
-    mla_plan, mla_tile_rows, mla_get_metadata, mla_decode_paged
+    mla_plan, mla_tile_rows, mla_get_metadata, mla_decode_paged,
+    mla_decode_splitkv + mla_combine_splits (the two stages of mla_decode_paged)
 The two-call FlashMLA-style API ("OpenSourceWeek Day 1 -- Demystifying
 DeepSeek's FlashMLA", deepseekonline.chat, §V.2):
     get_mla_metadata(cache_seqlens, s_q * h_q // h_kv, h_kv) -> (tile_metadata, num_splits)
@@ -24,7 +25,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "MlaError", "mla_plan", "mla_tile_rows", "mla_get_metadata", "mla_decode_paged",
-    "get_mla_metadata", "flash_mla_with_kvcache",
+    "mla_decode_splitkv", "mla_combine_splits", "get_mla_metadata", "flash_mla_with_kvcache",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -52,9 +53,11 @@ def _load() -> ctypes.CDLL:
     lib.mla_tile_rows.restype = I
     lib.mla_get_metadata.argtypes = [P, I, I, I, I, P, P, P]
     lib.mla_get_metadata.restype = I
-    lib.mla_decode_paged.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
-                                     ctypes.c_float, P, P, P, SZ, P]
-    lib.mla_decode_paged.restype = I
+    for name in ("mla_decode_paged", "mla_decode_splitkv", "mla_combine_splits"):
+        fn = getattr(lib, name)
+        fn.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
+                       ctypes.c_float, P, P, P, SZ, P]
+        fn.restype = I
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
     return lib
@@ -97,26 +100,34 @@ def mla_plan(batch: int, rows_per_kv: int, h_kv: int, dv: int = DV, num_cus: int
 
 
 def mla_get_metadata(cache_seqlens: torch.Tensor, rows_per_kv: int, h_kv: int,
-                     num_parts: Optional[int] = None, num_cus: int = 0):
-    """Split-KV schedule: (tile_metadata int32 [P, 8], num_splits int32 [b + 1])."""
+                     num_parts: Optional[int] = None, num_cus: int = 0, out=None):
+    """Split-KV schedule: (tile_metadata int32 [P, 8], num_splits int32 [b + 1]).
+
+    ``out`` may pass preallocated (tile_metadata, num_splits) tensors."""
     _require(cache_seqlens, "cache_seqlens", torch.int32)
     b = cache_seqlens.numel()
-    if num_parts is None:
-        num_parts, _ = mla_plan(b, rows_per_kv, h_kv, DV, num_cus)
     dev = cache_seqlens.device
-    md = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
-    ns = torch.empty((b + 1,), dtype=torch.int32, device=dev)
+    if out is not None:
+        md, ns = out
+        _require(md, "tile_metadata", torch.int32)
+        _require(ns, "num_splits", torch.int32)
+        if md.dim() != 2 or md.shape[1] != 8 or ns.numel() != b + 1:
+            raise ValueError("tile_metadata must be [P, 8] and num_splits [b + 1]")
+        if num_parts is not None and num_parts != md.shape[0]:
+            raise ValueError("num_parts does not match tile_metadata")
+        num_parts = md.shape[0]
+    else:
+        if num_parts is None:
+            num_parts, _ = mla_plan(b, rows_per_kv, h_kv, DV, num_cus)
+        md = torch.empty((num_parts, 8), dtype=torch.int32, device=dev)
+        ns = torch.empty((b + 1,), dtype=torch.int32, device=dev)
     _check(_lib.mla_get_metadata(cache_seqlens.data_ptr(), b, int(rows_per_kv), int(h_kv),
                                  int(num_parts), md.data_ptr(), ns.data_ptr(), _stream(dev)))
     return md, ns
 
 
-def mla_decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
-                     cache_seqlens: torch.Tensor, dv: int, tile_metadata: torch.Tensor,
-                     num_splits: torch.Tensor, causal: bool, softmax_scale: float,
-                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None):
-    """Paged decode; returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q])."""
+def _decode_call(fn, q, kcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,
+                 softmax_scale, out, lse, workspace):
     _require(q, "q", torch.bfloat16)
     _require(kcache, "kcache", torch.bfloat16)
     _require(block_table, "block_table", torch.int32)
@@ -140,16 +151,38 @@ def mla_decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.T
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
     _require(out, "out", torch.bfloat16)
     _require(lse, "lse", torch.float32)
-    need = (b + num_parts) * h_kv * rows * (dv + 1) * 4
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    _check(_lib.mla_decode_paged(
-        q.data_ptr(), kcache.data_ptr(), num_pages, block_table.data_ptr(), block_table.shape[1],
-        cache_seqlens.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
-        num_parts, num_splits.data_ptr(), int(bool(causal)), float(softmax_scale),
-        out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _stream(dev)))
+        workspace = torch.empty((b + num_parts) * h_kv * rows * (dv + 1) * 4, dtype=torch.uint8, device=dev)
+    _check(fn(q.data_ptr(), kcache.data_ptr(), num_pages, block_table.data_ptr(), block_table.shape[1],
+              cache_seqlens.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
+              num_parts, num_splits.data_ptr(), int(bool(causal)), float(softmax_scale),
+              out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+              workspace.numel() * workspace.element_size(), _stream(dev)))
     return out, lse
+
+
+def mla_decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                     cache_seqlens: torch.Tensor, dv: int, tile_metadata: torch.Tensor,
+                     num_splits: torch.Tensor, causal: bool, softmax_scale: float,
+                     out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Paged decode; returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q])."""
+    return _decode_call(_lib.mla_decode_paged, q, kcache, block_table, cache_seqlens, dv, tile_metadata,
+                        num_splits, causal, softmax_scale, out, lse, workspace)
+
+
+def mla_decode_splitkv(q, kcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,
+                       softmax_scale, out, lse, workspace):
+    """Decode kernel only (split sequences leave partials in ``workspace``)."""
+    return _decode_call(_lib.mla_decode_splitkv, q, kcache, block_table, cache_seqlens, dv, tile_metadata,
+                        num_splits, causal, softmax_scale, out, lse, workspace)
+
+
+def mla_combine_splits(q, kcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,
+                       softmax_scale, out, lse, workspace):
+    """LSE combine of the partials mla_decode_splitkv left in ``workspace``."""
+    return _decode_call(_lib.mla_combine_splits, q, kcache, block_table, cache_seqlens, dv, tile_metadata,
+                        num_splits, causal, softmax_scale, out, lse, workspace)
 
 
 def get_mla_metadata(cache_seqlens: torch.Tensor, num_heads_per_head_k: int, num_heads_k: int):

@@ -93,11 +93,18 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int rows_per_kv, i
   return ok();
 }
 
-int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages, const int32_t* block_table,
-                     int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
-                     int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
-                     const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+enum Stage { kDecode = 1, kCombine = 2 };
+
+int decode_common(int stages, const void* q, const void* kcache, int64_t num_pages,
+                  const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch,
+                  int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                  const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
+                  float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                  void* stream) {
   if (!q || !kcache || !block_table || !cache_seqlens || !tile_metadata || !num_splits || !out || !lse)
     return fail(MLA_ERR_INVALID, "null pointer argument");
   if (d_qk != MLA_D_QK) return fail(MLA_ERR_UNSUPPORTED, "d_qk must be %d (got %d)", MLA_D_QK, d_qk);
@@ -153,11 +160,49 @@ int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages, const
   p.xcd_map = (p.m_tiles * h_kv > 1 && num_parts % 8 == 0) ? 1 : 0;
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = mla::launch_decode(p, st);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  e = mla::launch_combine(p, st);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (stages & kDecode) {
+    hipError_t e = mla::launch_decode(p, st);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  if (stages & kCombine) {
+    hipError_t e = mla::launch_combine(p, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages, const int32_t* block_table,
+                     int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                     int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                     const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kDecode | kCombine, q, kcache, num_pages, block_table, max_blocks, cache_seqlens,
+                       batch, s_q, h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts,
+                       num_splits, causal, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_splitkv(const void* q, const void* kcache, int64_t num_pages, const int32_t* block_table,
+                       int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                       int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                       const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kDecode, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+                       h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
+                       softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages, const int32_t* block_table,
+                       int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                       int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                       const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kCombine, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+                       h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
+                       softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

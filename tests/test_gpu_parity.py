@@ -214,3 +214,47 @@ def test_out_of_range_page_ids_are_safe(env):
     go, gl = as_np(out, lse)
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
     del torch
+
+
+# ------------------------------------------------------------------ HIP graphs
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_graph_replay_matches_eager(env, cfg):
+    """A captured step (metadata + decode + combine) replayed several times, with
+    eager work and synchronisations between replays, matches the eager result
+    bit for bit on every replay."""
+    torch, mla, _, dev = env
+    w = workloads.config_workload(cfg)
+    q, kc, bt, sl = upload(torch, w, dev)
+    P, ws_bytes = mla.mla_plan(w.batch, w.rows, w.h_kv)
+    md = torch.empty((P, 8), dtype=torch.int32, device=dev)
+    ns = torch.empty((w.batch + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.s_q, w.h_q, w.dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+
+    def step():
+        mla.mla_get_metadata(sl, w.rows, w.h_kv, num_parts=P, out=(md, ns))
+        mla.mla_decode_paged(q, kc, bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.zero_()
+        lse.fill_(7.0)
+        ws.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {r}: out differs"
+        assert torch.equal(lse, ref_lse), f"replay {r}: lse differs"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
