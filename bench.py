@@ -64,18 +64,26 @@ def source_digest():
 
 
 def traffic_from_profiles(workload, launch_kind):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when missing or taken on a different version of the kernel."""
-    path = os.path.join(ROOT, "profiles", "decode_counters.json")
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (profiles/decode_hbm_traffic.md), or None when missing or taken on a
+    different version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "decode_hbm_traffic.md")
     try:
         with open(path) as fh:
-            data = json.load(fh)
-    except (OSError, ValueError):
+            lines = fh.read().splitlines()
+    except OSError:
         return None
-    rec = data.get(workload)
-    if not rec or rec.get("kernel_digest") != source_digest() or rec.get("launch") != launch_kind:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    digest = source_digest()
+    for ln in lines:
+        cells = [c.strip() for c in ln.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] == workload and cells[2] == launch_kind:
+            if cells[1] != digest:
+                return None
+            try:
+                return int(float(cells[5]))
+            except ValueError:
+                return None
+    return None
 
 
 def cpu_baseline(w, bytes_step, target_s):
@@ -109,6 +117,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -128,6 +138,16 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b_ = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            b_.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
     cfg = workloads.CONFIGS[args.config]
     w = workloads.config_workload(args.config)
     bytes_step, flops_step, kv_bytes = algorithmic(w)

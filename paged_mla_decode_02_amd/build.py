@@ -31,7 +31,10 @@ def common_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
             "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
             # packed fp32 VALU forms are kept out of the generated code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA accumulators in VGPRs: the online-softmax rescale and the
+            # epilogue scale them with VALU ops, and the AGPR form duplicates them
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def _compile(src: str) -> str:

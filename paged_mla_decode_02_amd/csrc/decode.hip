@@ -167,13 +167,19 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b, int 
   return r;
 }
 
-// Resource descriptor for page `blk` of sequence b: the page's bytes for this
-// layout, clipped to the valid tokens so slots past L (and unknown page ids)
-// read as zeros.
-__device__ __forceinline__ i32x4_t page_rsrc(const DecodeParams& p, int b, int blk, int L) {
-  const int pid = blk < p.max_blocks
-                      ? __builtin_amdgcn_readfirstlane(p.block_table[(long long)b * p.max_blocks + blk])
-                      : -1;
+// Block-table entries of pages [base, base + 64) of sequence b, one per lane
+// (-1 past `hi` or the table); a page's id is then read with readlane, so the
+// DMA for a page never waits on a dependent global load.
+__device__ __forceinline__ int load_page_ids(const DecodeParams& p, int b, int base, int hi, int lane) {
+  const int j = base + lane;
+  return (j < hi && j < p.max_blocks) ? p.block_table[(long long)b * p.max_blocks + j] : -1;
+}
+__device__ __forceinline__ int page_id(int ids, int k) { return __builtin_amdgcn_readlane(ids, k); }
+
+// Resource descriptor for page `blk` (physical id pid) of a sequence of length
+// L: the page's bytes for this layout, clipped to the valid tokens so slots past
+// L (and unknown page ids) read as zeros.
+__device__ __forceinline__ i32x4_t page_rsrc(const DecodeParams& p, int pid, int blk, int L) {
   int valid = L - blk * kPage;
   if (valid > kPage) valid = kPage;
   const bool ok = pid >= 0 && (long long)pid < p.num_pages;
@@ -284,11 +290,14 @@ decode_tokensplit(DecodeParams p) {
     float m_run = -INFINITY, l_run = 0.f;
 
     const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
-    if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, b, sr.lo, sr.L), dma);
+    int ids = load_page_ids(p, b, sr.lo, sr.hi, lane);
+    if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
       const int st = (blk - sr.lo) & 1;
       if (blk + 1 < sr.hi) {
-        dma_slice(slices + (st ^ 1) * kSliceBytes, page_rsrc(p, b, blk + 1, sr.L), dma);
+        const int k = (blk + 1 - sr.lo) & 63;
+        if (k == 0) ids = load_page_ids(p, b, blk + 1, sr.hi, lane);
+        dma_slice(slices + (st ^ 1) * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L), dma);
         wait_vmcnt<kSliceDma>();
       } else {
         wait_vmcnt<0>();
@@ -296,13 +305,30 @@ decode_tokensplit(DecodeParams p) {
       const LDS_AS char* reg = slices + st * kSliceBytes;
 
       // S^T[16 tokens x 16 rows] = K_slice . Q^T ; A-operand row = token r16,
-      // chunk 4*ks + grp = group ks/2, position 4*(ks&1) + grp
-      f32x4_t S = {0.f, 0.f, 0.f, 0.f};
+      // chunk 4*ks + grp = group ks/2, position 4*(ks&1) + grp.  Three
+      // accumulation chains; K operands are read kAhead k-steps ahead.
+      f32x4_t S;
+      {
+        constexpr int kAhead = 4;
+        f32x4_t Sc[3] = {};
+        bf16x8_t ka[kAhead + 1];
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const bf16x8_t a = *(const LDS_AS bf16x8_t*)(reg + kaddr[ks & 1] + (ks >> 1) * kGroupBytes);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[ks], S, 0, 0, 0);
+        for (int i = 0; i < kAhead; ++i)
+          ka[i] = *(const LDS_AS bf16x8_t*)(reg + kaddr[i & 1] + (i >> 1) * kGroupBytes);
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          if (ks + kAhead < 18) {
+            const int n = ks + kAhead;
+            ka[n % (kAhead + 1)] = *(const LDS_AS bf16x8_t*)(reg + kaddr[n & 1] + (n >> 1) * kGroupBytes);
+          }
+          Sc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks % (kAhead + 1)], qreg[ks], Sc[ks % 3], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks + kAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        S = Sc[0] + Sc[1] + Sc[2];
       }
+      __builtin_amdgcn_sched_barrier(0);
       // online softmax over this wave's 16 tokens: lane holds tokens grp*4 + i of row r16
       const int tok0 = blk * kPage + w * kSlice + grp * 4;
       float x[4];
@@ -334,14 +360,29 @@ decode_tokensplit(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) O[i] *= alpha;
       }
+      __builtin_amdgcn_sched_barrier(0);
       // O^T[16 dims x 16 rows] += V^T[16 dims x 16 tokens] . P^T, 32 dim tiles;
-      // dims 16*dt + (lane&3)*4 = group dt/4, position 2*(dt&3) + (lane&3)/2
+      // dims 16*dt + (lane&3)*4 = group dt/4, position 2*(dt&3) + (lane&3)/2.
+      // Transposed reads run kVAhead tiles ahead of their MFMA.
+      {
+        constexpr int kVAhead = 8;
+        bf16x4_t va[kVAhead + 1];
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const bf16x4_t a = lds_tr16(reg + vaddr[dt & 3] + (dt >> 2) * kGroupBytes);
-        O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), pbs,
-                                                          O[dt], 0, 0, 0);
+        for (int i = 0; i < kVAhead; ++i) va[i] = lds_tr16(reg + vaddr[i & 3] + (i >> 2) * kGroupBytes);
+        __builtin_amdgcn_sched_group_barrier(0x100, kVAhead, 0);
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) {
+          if (dt + kVAhead < 32) {
+            const int n = dt + kVAhead;
+            va[n % (kVAhead + 1)] = lds_tr16(reg + vaddr[n & 3] + (n >> 2) * kGroupBytes);
+          }
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, va[dt % (kVAhead + 1)]),
+                                                            pbs, O[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (dt + kVAhead < 32) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- merge the four waves' partial softmax states (LDS), then write
@@ -519,13 +560,18 @@ decode_pairsplit(DecodeParams p) {
     for (int dt = 0; dt < 4; ++dt) O[dt][0] = O[dt][1] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;  // l_run covers this wave's token group only
 
-    if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, b, sr.lo, sr.L), dma);
+    int ids = load_page_ids(p, b, sr.lo, sr.hi, lane);
+    if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
       const int pb = (blk - sr.lo) & 1;
       wait_vmcnt<0>();
       wg_barrier();  // page blk visible; the other buffer, P and xmax are free
-      if (blk + 1 < sr.hi)
-        dma_slice(pages + (pb ^ 1) * kPageBytes + w * kSliceBytes, page_rsrc(p, b, blk + 1, sr.L), dma);
+      if (blk + 1 < sr.hi) {
+        const int k = (blk + 1 - sr.lo) & 63;
+        if (k == 0) ids = load_page_ids(p, b, blk + 1, sr.hi, lane);
+        dma_slice(pages + (pb ^ 1) * kPageBytes + w * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L),
+                  dma);
+      }
       const LDS_AS char* page = pages + pb * kPageBytes;
 
       // ---- S^T[32 tokens x 32 rows] = K . Q^T, two accumulation chains,
@@ -533,20 +579,22 @@ decode_pairsplit(DecodeParams p) {
       f32x16_t S;
       {
         f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
-        bf16x8_t ka[4];
+        constexpr int kAhead = 4;  // K operands in flight ahead of the MFMA that uses them
+        bf16x8_t ka[kAhead + 1];
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
+        for (int i = 0; i < kAhead; ++i)
           ka[i] = *(const LDS_AS bf16x8_t*)(page + kaddr[i & 3] + (i >> 2) * kGroupBytes);
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
-          if (ks + 3 < 36) {
-            const int n = ks + 3;
-            ka[n & 3] = *(const LDS_AS bf16x8_t*)(page + kaddr[n & 3] + (n >> 2) * kGroupBytes);
+          if (ks + kAhead < 36) {
+            const int n = ks + kAhead;
+            ka[n % (kAhead + 1)] = *(const LDS_AS bf16x8_t*)(page + kaddr[n & 3] + (n >> 2) * kGroupBytes);
           }
-          if (ks & 1) S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3], qreg[ks], S1, 0, 0, 0);
-          else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks & 3], qreg[ks], S0, 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (ks & 1) S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S1, 0, 0, 0);
+          else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S0, 0, 0, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         S = S0 + S1;
       }
@@ -598,20 +646,43 @@ decode_pairsplit(DecodeParams p) {
           }
         }
       }
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8_t bp0 = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
-        const bf16x8_t bp1 = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
+      // operands of k-step ks (16 tokens): P^T for both row tiles and V^T for the
+      // four 32-dim tiles; the next k-step's operands load while this one's
+      // MFMAs run
+      struct PvOps {
+        bf16x8_t bp[2];
+        bf16x8_t va[4];
+      };
+      auto load_ops = [&](int ks) {
+        PvOps o;
+        o.bp[0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
+        o.bp[1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
         const LDS_AS char* vs = page + ks * kSliceBytes;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int go = (dt >> 1) * kGroupBytes;
           const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
           const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
-          const bf16x8_t a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp0, O[dt][0], 0, 0, 0);
-          O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp1, O[dt][1], 0, 0, 0);
+          o.va[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+        return o;
+      };
+      PvOps ops[2];
+      ops[0] = load_ops(0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) {
+          ops[(ks + 1) & 1] = load_ops(ks + 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+        }
+        const PvOps& o = ops[ks & 1];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
+          O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
