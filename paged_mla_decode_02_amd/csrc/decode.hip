@@ -59,9 +59,6 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4_t rsrc, LDS_AS void* lds, int size,
-                                                           int voffset, int soffset, int offset,
-                                                           int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 constexpr int kThreads = 256;
 constexpr int kSlice = 16;                         // tokens one wave moves per page
@@ -143,7 +140,7 @@ __device__ __forceinline__ void map_block(const DecodeParams& p, int& part, int&
 }
 
 struct SeqRange {
-  int L, nb, lo, hi, ord, chunks;
+  int L, nb, lo, hi, ord, chunks, base;  // base: first workspace slot of the sequence
   bool ok;
 };
 
@@ -159,20 +156,23 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b, int 
   if (r.lo < 0) r.lo = 0;
   if (r.lo > r.hi) r.lo = r.hi;
   r.ord = (b == i0) ? ord0 : 0;
-  r.chunks = p.num_splits[b + 1] - p.num_splits[b];
+  r.base = p.num_splits[b];
+  r.chunks = p.num_splits[b + 1] - r.base;
   // metadata that does not belong to these lengths / part count must not make
   // the epilogue write outside the workspace: such a chunk writes nothing
-  const long long slot = (long long)p.num_splits[b] + r.ord;
+  const long long slot = (long long)r.base + r.ord;
   r.ok = r.ord >= 0 && r.ord < r.chunks && slot >= 0 && slot < (long long)p.batch + p.num_parts;
   return r;
 }
 
 // Block-table entries of pages [base, base + 64) of sequence b, one per lane
-// (-1 past `hi` or the table); a page's id is then read with readlane, so the
-// DMA for a page never waits on a dependent global load.
-__device__ __forceinline__ int load_page_ids(const DecodeParams& p, int b, int base, int hi, int lane) {
+// (-1 past the table); a page's id is then read with readlane, so the DMA for a
+// page never waits on a dependent global load.  Entries past the sequence's
+// last page are read (in bounds of the table) but never used, which lets the
+// load start before the sequence length is known.
+__device__ __forceinline__ int load_page_ids(const DecodeParams& p, int b, int base, int lane) {
   const int j = base + lane;
-  return (j < hi && j < p.max_blocks) ? p.block_table[(long long)b * p.max_blocks + j] : -1;
+  return j < p.max_blocks ? p.block_table[(long long)b * p.max_blocks + j] : -1;
 }
 __device__ __forceinline__ int page_id(int ids, int k) { return __builtin_amdgcn_readlane(ids, k); }
 
@@ -204,14 +204,25 @@ __device__ __forceinline__ SliceDma slice_dma_offsets(int tok0, int kvh, int h_k
   }
   return d;
 }
-// The instruction's immediate offset would move the LDS destination as well, so
-// the group's source offset goes into the per-lane offset instead.
+// One 1 KB HBM -> LDS transfer: 16 bytes per lane from rsrc + voffset to LDS
+// dst + 16 * lane.  Written as inline assembly so the compiler does not track
+// it: it would otherwise treat every later LDS read as possibly aliasing the
+// transfer in flight and wait for all outstanding loads before it, which
+// serialises the page pipeline; the kernels wait for their transfers explicitly
+// (wait_vmcnt) before reading the LDS they fill.  The instruction has no
+// register result.  M0 holds the LDS base; one wait state separates its write
+// from the transfer that reads it.  The immediate offset would move the LDS
+// destination as well, so the source offset is all in voffset.
+__device__ __forceinline__ void dma16(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"((unsigned)(size_t)dst), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
 template <int G>
 __device__ __forceinline__ void dma_group(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d) {
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (LDS_AS void*)(dst + G * kGroupBytes), 16, d.vbase[0] + G * 128,
-                                  0, 0, 0);
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (LDS_AS void*)(dst + G * kGroupBytes + 1024), 16,
-                                  d.vbase[1] + G * 128, 0, 0, 0);
+  dma16(dst + G * kGroupBytes, rsrc, d.vbase[0] + G * 128);
+  dma16(dst + G * kGroupBytes + 1024, rsrc, d.vbase[1] + G * 128);
 }
 template <int... Gs>
 __device__ __forceinline__ void dma_groups(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d,
@@ -233,6 +244,11 @@ __device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh
 
 // ---------------------------------------------------------------------------
 // <= 16 rows: token-split kernel.
+// The part's pages form one stream across its sequences: while a page is
+// processed the next one of the stream -- possibly the first page of the next
+// sequence -- is on its way into the other LDS buffer, and the next sequence's
+// length and page ids load while the current one runs, its queries during the
+// current one's epilogue.
 // LDS: per wave two 16-token slices (2 x 18432 B) + merge statistics.
 constexpr int kTsLds = 4 * 2 * kSliceBytes + 4 * 16 * 2 * 4;
 
@@ -266,43 +282,63 @@ decode_tokensplit(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) vaddr[k] = slice_off(tt, 2 * k + ((lane & 3) >> 1)) + ((lane & 1) << 3);
   }
+  const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
 
-  for (int b = i0; b <= j0; ++b) {
-    const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
+  // queries: B operand of the 16x16x32 QK MFMA, 8 dims per lane per k-step.
+  // Rows past the last one (a ragged tile) compute on row 0's query; every row
+  // is independent through the softmax and PV, and such rows are never stored,
+  // so the loads need no mask and nothing waits for them before first use.
+  bf16x8_t qreg[18];
+  auto load_q = [&](int bq) {
+    int s;
+    long long qo;
+    row_coords(p, bq, kvh, row_ok ? row : 0, s, qo);
+    const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk) + grp;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qreg[ks] = qp[ks * 4];
+  };
+
+  // in-flight DMA only ever targets buffer `buf`; buf ^ 1 is free between pages
+  int buf = 0;
+  int b = i0;
+  int ids = load_page_ids(p, b, b == i0 ? f0 : 0, lane);
+  SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
+  if (sr.lo != f0) ids = load_page_ids(p, b, sr.lo, lane);  // clamped (malformed) metadata
+  load_q(b);
+  if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+  for (;;) {
+    const bool has_next = b < j0;
+    SeqRange nr = {};
+    int nids = -1;
+    if (has_next) {
+      nids = load_page_ids(p, b + 1, 0, lane);
+      nr = seq_range(p, b + 1, i0, f0, j0, e0, ord0);
+    }
     int s;
     long long qo;
     row_coords(p, b, kvh, row_ok ? row : 0, s, qo);
     const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
 
-    // queries: B operand of the 16x16x32 QK MFMA, 8 dims per lane per k-step
-    bf16x8_t qreg[18];
-    {
-      const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk) + grp;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        bf16x8_t v = qp[ks * 4];
-        qreg[ks] = row_ok ? v : bf16x8_t{};
-      }
-    }
     f32x4_t O[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) O[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
-    int ids = load_page_ids(p, b, sr.lo, sr.hi, lane);
-    if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+    bool next_started = false;  // first page of the next sequence already requested
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
-      const int st = (blk - sr.lo) & 1;
       if (blk + 1 < sr.hi) {
         const int k = (blk + 1 - sr.lo) & 63;
-        if (k == 0) ids = load_page_ids(p, b, blk + 1, sr.hi, lane);
-        dma_slice(slices + (st ^ 1) * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L), dma);
+        if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
+        dma_slice(slices + (buf ^ 1) * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L), dma);
+        wait_vmcnt<kSliceDma>();
+      } else if (has_next && nr.lo < nr.hi) {
+        dma_slice(slices + (buf ^ 1) * kSliceBytes, page_rsrc(p, page_id(nids, 0), nr.lo, nr.L), dma);
+        next_started = true;
         wait_vmcnt<kSliceDma>();
       } else {
         wait_vmcnt<0>();
       }
-      const LDS_AS char* reg = slices + st * kSliceBytes;
+      const LDS_AS char* reg = slices + buf * kSliceBytes;
 
       // S^T[16 tokens x 16 rows] = K_slice . Q^T ; A-operand row = token r16,
       // chunk 4*ks + grp = group ks/2, position 4*(ks&1) + grp.  Three
@@ -383,9 +419,14 @@ decode_tokensplit(DecodeParams p) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      buf ^= 1;
     }
+    // the next sequence's queries load during this epilogue
+    if (has_next) load_q(b + 1);
 
-    // ---- merge the four waves' partial softmax states (LDS), then write
+    // ---- merge the four waves' partial softmax states through LDS (the
+    // buffer just consumed, buf ^ 1, of every wave), then write
+    const int dbuf = (buf ^ 1) * kSliceBytes;
     wg_barrier();  // every wave is done with its slices
     if (lane < 16) {
       mstat[(w * 16 + lane) * 2 + 0] = m_run;
@@ -416,12 +457,11 @@ decode_tokensplit(DecodeParams p) {
     long long ro;
     row_coords(p, b, kvh, rrow < p.rows ? rrow : 0, rs, ro);
     const bool split = sr.chunks > 1;
-    const long long slot_row =
-        (((long long)(p.num_splits[b] + sr.ord) * p.h_kv + kvh) * p.rows + rrow);
+    const long long slot_row = ((long long)(sr.base + sr.ord) * p.h_kv + kvh) * p.rows + rrow;
     constexpr int kDumpStride = 260;  // floats per row: 256 + 4 pad
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      LDS_AS float* dump = (LDS_AS float*)slices;
+      LDS_AS float* dump = (LDS_AS float*)(slices + dbuf);
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
         *(LDS_AS f32x4_t*)(dump + r16 * kDumpStride + dt * 16 + grp * 4) = O[half * 16 + dt];
@@ -429,7 +469,7 @@ decode_tokensplit(DecodeParams p) {
       f32x4_t acc[4] = {};
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const LDS_AS float* src = (const LDS_AS float*)(smem + v * 2 * kSliceBytes);
+        const LDS_AS float* src = (const LDS_AS float*)(smem + v * 2 * kSliceBytes + dbuf);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           acc[k] += *(const LDS_AS f32x4_t*)(src + rr * kDumpStride + w * 64 + (lane & 3) * 16 + k * 4);
@@ -460,6 +500,13 @@ decode_tokensplit(DecodeParams p) {
       if (split) p.lse_acc[slot_row] = l2;
       else p.lse[ro] = l2 * kLn2;
     }
+    if (!has_next) break;
+    // advance the stream; an empty sequence requested nothing, so its successor
+    // starts its own first page now (buffer `buf`, idle)
+    ++b;
+    sr = nr;
+    ids = nids;
+    if (!next_started && sr.lo < sr.hi) dma_slice(slices + buf * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
   }
 }
 
@@ -546,21 +593,19 @@ decode_pairsplit(DecodeParams p) {
     row_coords(p, b, kvh, qrow_ok ? qrow : 0, s, qo);
     const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
 
+    // rows past the last one compute on row 0's query and are never stored
     bf16x8_t qreg[36];
     {
       const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk) + hb;
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks) {
-        bf16x8_t v = qp[ks * 2];
-        qreg[ks] = qrow_ok ? v : bf16x8_t{};
-      }
+      for (int ks = 0; ks < 36; ++ks) qreg[ks] = qp[ks * 2];
     }
     f32x16_t O[4][2];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) O[dt][0] = O[dt][1] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;  // l_run covers this wave's token group only
 
-    int ids = load_page_ids(p, b, sr.lo, sr.hi, lane);
+    int ids = load_page_ids(p, b, sr.lo, lane);
     if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
       const int pb = (blk - sr.lo) & 1;
@@ -568,7 +613,7 @@ decode_pairsplit(DecodeParams p) {
       wg_barrier();  // page blk visible; the other buffer, P and xmax are free
       if (blk + 1 < sr.hi) {
         const int k = (blk + 1 - sr.lo) & 63;
-        if (k == 0) ids = load_page_ids(p, b, blk + 1, sr.hi, lane);
+        if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
         dma_slice(pages + (pb ^ 1) * kPageBytes + w * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L),
                   dma);
       }
@@ -694,7 +739,7 @@ decode_pairsplit(DecodeParams p) {
     }
     wg_barrier();
     const bool split = sr.chunks > 1;
-    const long long slot = (long long)(p.num_splits[b] + sr.ord) * p.h_kv + kvh;
+    const long long slot = (long long)(sr.base + sr.ord) * p.h_kv + kvh;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int rl = rt * 32 + l32;

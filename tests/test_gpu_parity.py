@@ -221,7 +221,8 @@ def test_out_of_range_page_ids_are_safe(env):
 def test_graph_replay_matches_eager(env, cfg):
     """A captured step (metadata + decode + combine) replayed several times, with
     eager work and synchronisations between replays, matches the eager result
-    bit for bit on every replay."""
+    bit for bit on every replay.  The workspace is refilled with NaNs between
+    replays: partials of an earlier call must never be read."""
     torch, mla, _, dev = env
     w = workloads.config_workload(cfg)
     q, kc, bt, sl = upload(torch, w, dev)
@@ -250,7 +251,7 @@ def test_graph_replay_matches_eager(env, cfg):
     for r in range(4):
         out.zero_()
         lse.fill_(7.0)
-        ws.zero_()
+        ws.fill_(255)
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out), f"replay {r}: out differs"
