@@ -224,6 +224,14 @@ __device__ __forceinline__ void dma_group(LDS_AS char* dst, i32x4_t rsrc, const 
   dma16(dst + G * kGroupBytes, rsrc, d.vbase[0] + G * 128);
   dma16(dst + G * kGroupBytes + 1024, rsrc, d.vbase[1] + G * 128);
 }
+// Piece i (0..17) of a slice transfer: chunk group i / 2, token half i % 2.
+// Lets a kernel spread a slice's transfers over its compute instead of issuing
+// them back to back: a burst of transfers stalls the issuing wave for as long
+// as the memory pipeline takes to accept them.
+__device__ __forceinline__ void dma_piece(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d, int i) {
+  const int g = i >> 1, th = i & 1;
+  dma16(dst + g * kGroupBytes + th * 1024, rsrc, d.vbase[th] + g * 128);
+}
 template <int... Gs>
 __device__ __forceinline__ void dma_groups(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d,
                                            std::integer_sequence<int, Gs...>) {
@@ -526,6 +534,11 @@ constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
 constexpr int kPsAbuf = kPsXmax + 2 * kPsRows * 4;
 constexpr int kPsSbuf = kPsAbuf + kPsRows * 4;
 constexpr int kPsLds = kPsSbuf + 2 * kPsRows * 2 * 4;
+// transfer pieces of the next page issued during QK^T (the rest during PV)
+#ifndef MLA_QK_DMA
+#define MLA_QK_DMA 18
+#endif
+constexpr int kQkDma = MLA_QK_DMA;
 
 // P row r holds 64 bf16 tokens as 8 chunks of 16 bytes; chunk c is stored at
 // position c ^ ((r >> 1) & 7), which keeps 16 consecutive rows reading the same
@@ -611,11 +624,15 @@ decode_pairsplit(DecodeParams p) {
       const int pb = (blk - sr.lo) & 1;
       wait_vmcnt<0>();
       wg_barrier();  // page blk visible; the other buffer, P and xmax are free
-      if (blk + 1 < sr.hi) {
+      // the next page's slice moves in pieces spread over this page's MFMAs:
+      // kQkDma pieces during QK^T, the rest during PV
+      const bool has_next = blk + 1 < sr.hi;
+      LDS_AS char* ndst = pages + (pb ^ 1) * kPageBytes + w * kSliceBytes;
+      i32x4_t nrsrc = {0, 0, 0, 0};
+      if (has_next) {
         const int k = (blk + 1 - sr.lo) & 63;
         if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
-        dma_slice(pages + (pb ^ 1) * kPageBytes + w * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L),
-                  dma);
+        nrsrc = page_rsrc(p, page_id(ids, k), blk + 1, sr.L);
       }
       const LDS_AS char* page = pages + pb * kPageBytes;
 
@@ -640,6 +657,9 @@ decode_pairsplit(DecodeParams p) {
           else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S0, 0, 0, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (has_next) {
+            for (int i = ks * kQkDma / 36; i < (ks + 1) * kQkDma / 36; ++i) dma_piece(ndst, nrsrc, dma, i);
+          }
         }
         S = S0 + S1;
       }
@@ -728,6 +748,10 @@ decode_pairsplit(DecodeParams p) {
           O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        if (has_next) {
+          for (int i = kQkDma + ks * (kSliceDma - kQkDma) / 4; i < kQkDma + (ks + 1) * (kSliceDma - kQkDma) / 4; ++i)
+            dma_piece(ndst, nrsrc, dma, i);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
