@@ -21,7 +21,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRowsPerBlock = 2;
-constexpr int kThreadsPerRow = kDv / 4;  // 4 dims per thread
+constexpr int kThreadsPerRow = kDv / 4;  // 4 dims per thread, two waves per row
+constexpr int kTile = 256;               // chunk weights staged in LDS at a time
+constexpr int kUnroll = 8;               // partial loads in flight per thread
+constexpr int kFew = 8;                  // up to this many chunks: single-pass path
+static_assert(kFew == 8, "combine_few is instantiated for 2..8 chunks");
+struct LDS_float_pair {
+  float v[2];
+};
 constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
@@ -29,40 +36,134 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Few chunks: every thread reads the row's NC lse values itself and all NC
+// partial quads at once (two dependent loads in all, no barrier).
+template <int NC>
+__device__ __forceinline__ void combine_few(const DecodeParams& p, long long r0, long long stride, long long o,
+                                            int d0, bool write_lse) {
+  float l[NC];
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < NC; ++s) {
+    l[s] = p.lse_acc[r0 + s * stride];
+    M = fmaxf(M, l[s]);
+  }
+  f32x4_t v[NC];
+#pragma unroll
+  for (int s = 0; s < NC; ++s) v[s] = *(const f32x4_t*)(p.o_acc + (r0 + s * stride) * kDv + d0);
+  float wsum = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < NC; ++s) {
+      const float wgt = (l[s] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l[s] - M);
+      wsum += wgt;
+      acc += wgt * v[s];
+    }
+    acc *= 1.f / wsum;
+  }
+  u32x2_t pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+  *(u32x2_t*)(p.out + o * kDv + d0) = pk;
+  if (write_lse) p.lse[o] = (M == -INFINITY) ? -INFINITY : (M + __builtin_amdgcn_logf(wsum)) * kLn2;
+}
+
+// Maximum and sum over the kThreadsPerRow threads (two waves) of one row.
+__device__ __forceinline__ float row_reduce(float v, bool is_max, LDS_float_pair* red, int rl, int wv) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const float u = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, u) : v + u;
+  }
+  if ((threadIdx.x & 63) == 0) red[rl].v[wv] = v;
+  __syncthreads();
+  const float r = is_max ? fmaxf(red[rl].v[0], red[rl].v[1]) : red[rl].v[0] + red[rl].v[1];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup merges kRowsPerBlock rows of one (sequence, KV head): each row's
+// 128 threads first reduce max_s l_s and sum_s 2^(l_s - M) over the chunks, then
+// normalised chunk weights go through LDS kTile at a time and every thread
+// accumulates its 4 dims over the chunks with kUnroll loads in flight.
 __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel(DecodeParams p) {
+  __shared__ float wts[kRowsPerBlock][kTile];
+  __shared__ LDS_float_pair red[kRowsPerBlock];
   const int b = blockIdx.x;
   const int kvh = blockIdx.z;
   const int base = p.num_splits[b];
   const int nsp = p.num_splits[b + 1] - base;
   if (nsp <= 1) return;  // written directly by the decode kernel
   if (base < 0 || (long long)base + nsp > (long long)p.batch + p.num_parts) return;  // foreign metadata
-  const int row = blockIdx.y * kRowsPerBlock + threadIdx.x / kThreadsPerRow;
-  if (row >= p.rows) return;
-  const int d0 = (threadIdx.x % kThreadsPerRow) * 4;
+  const int rl = threadIdx.x / kThreadsPerRow;
+  const int t = threadIdx.x % kThreadsPerRow;
+  const int wv = t / 64;
+  const int row = blockIdx.y * kRowsPerBlock + rl;
+  const bool row_ok = row < p.rows;  // uniform over the row's two waves
+  const int d0 = t * 4;
 
   const long long stride = (long long)p.h_kv * p.rows;  // rows between consecutive slots
-  const long long r0 = ((long long)base * p.h_kv + kvh) * p.rows + row;
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, p.lse_acc[r0 + s * stride]);
-
+  const long long r0 = ((long long)base * p.h_kv + kvh) * p.rows + (row_ok ? row : 0);
   const int sq = row / p.group;
   const int h = kvh * p.group + row % p.group;
   const long long o = ((long long)b * p.s_q + sq) * p.h_q + h;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsp; ++s) {
-      const float l = p.lse_acc[r0 + s * stride];
-      const float wgt = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M);
-      const f32x4_t v = *(const f32x4_t*)(p.o_acc + (r0 + s * stride) * kDv + d0);
-      acc += wgt * v;
-      wsum += wgt;
+
+  if (nsp <= kFew) {
+    if (!row_ok) return;
+    switch (nsp) {
+      case 2: combine_few<2>(p, r0, stride, o, d0, t == 0); break;
+      case 3: combine_few<3>(p, r0, stride, o, d0, t == 0); break;
+      case 4: combine_few<4>(p, r0, stride, o, d0, t == 0); break;
+      case 5: combine_few<5>(p, r0, stride, o, d0, t == 0); break;
+      case 6: combine_few<6>(p, r0, stride, o, d0, t == 0); break;
+      case 7: combine_few<7>(p, r0, stride, o, d0, t == 0); break;
+      default: combine_few<8>(p, r0, stride, o, d0, t == 0); break;
     }
-    acc *= 1.f / wsum;
+    return;
   }
+
+  float M = -INFINITY;
+  if (row_ok)
+    for (int s = t; s < nsp; s += kThreadsPerRow) M = fmaxf(M, p.lse_acc[r0 + s * stride]);
+  M = row_reduce(M, true, red, rl, wv);
+  float wsum = 0.f;
+  if (row_ok && M != -INFINITY)
+    for (int s = t; s < nsp; s += kThreadsPerRow) {
+      const float l = p.lse_acc[r0 + s * stride];
+      wsum += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M);
+    }
+  wsum = row_reduce(wsum, false, red, rl, wv);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsp; s0 += kTile) {
+    const int n = min(kTile, nsp - s0);
+    for (int j = t; j < kTile; j += kThreadsPerRow) {
+      float wgt = 0.f;
+      if (row_ok && j < n && M != -INFINITY) {
+        const float l = p.lse_acc[r0 + (s0 + j) * stride];
+        wgt = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M) * inv;
+      }
+      wts[rl][j] = wgt;
+    }
+    __syncthreads();
+    if (row_ok) {
+      const float* src = p.o_acc + (r0 + s0 * stride) * kDv + d0;
+      for (int j0 = 0; j0 < n; j0 += kUnroll) {
+        f32x4_t v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int j = min(j0 + u, n - 1);  // past the end: weight 0, any valid slot
+          v[u] = *(const f32x4_t*)(src + j * stride * kDv);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc += wts[rl][min(j0 + u, kTile - 1)] * (j0 + u < n ? v[u] : f32x4_t{});
+      }
+    }
+    __syncthreads();
+  }
+  if (!row_ok) return;
   u32x2_t pk = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
   *(u32x2_t*)(p.out + o * kDv + d0) = pk;
-  if (d0 == 0) p.lse[o] = (M == -INFINITY) ? -INFINITY : (M + __builtin_amdgcn_logf(wsum)) * kLn2;
+  if (t == 0) p.lse[o] = (M == -INFINITY) ? -INFINITY : (M + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
 }  // namespace
