@@ -40,6 +40,7 @@
 //     resident in registers), P goes through LDS, and PV is split by output dims
 //     (128 per wave), so each V element of a page is read from LDS once per
 //     workgroup.
+#include <type_traits>
 #include <utility>
 
 #include "mla_kernels.h"
@@ -637,9 +638,9 @@ decode_pairsplit(DecodeParams p) {
       const LDS_AS char* page = pages + pb * kPageBytes;
 
       // ---- S^T[32 tokens x 32 rows] = K . Q^T, two accumulation chains,
-      // K operands fetched three k-steps ahead
-      f32x16_t S;
-      {
+      // K operands fetched kAhead k-steps ahead.  The loop is instantiated with
+      // and without the next page's transfer pieces so that no branch splits it.
+      auto qk = [&](auto with_dma) {
         f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
         constexpr int kAhead = 4;  // K operands in flight ahead of the MFMA that uses them
         bf16x8_t ka[kAhead + 1];
@@ -657,12 +658,16 @@ decode_pairsplit(DecodeParams p) {
           else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S0, 0, 0, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if (has_next) {
+          if constexpr (decltype(with_dma)::value) {
+#pragma unroll
             for (int i = ks * kQkDma / 36; i < (ks + 1) * kQkDma / 36; ++i) dma_piece(ndst, nrsrc, dma, i);
           }
         }
-        S = S0 + S1;
-      }
+        return S0 + S1;
+      };
+      f32x16_t S;
+      if (has_next) S = qk(std::true_type{});
+      else S = qk(std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page
       const int tok0 = blk * kPage + 32 * tg + 4 * hb;
