@@ -184,7 +184,7 @@ int oracle_decode(const uint16_t* q, const uint16_t* kcache, long long num_pages
  * an empty part (lo >= T) is {b, 0, b, 0, 0, 0, 0, 0}.
  *
  * Tile rows and the constants: rows <= 16 -> 16, else 64 (the row tile one
- * workgroup owns); OVH = max(1, tile / 16); QMIN = 2 * OVH.
+ * workgroup owns); OVH = 3 for the 16-row tile, tile / 16 otherwise; QMIN = 2 * OVH.
  * Written with plain loops over all sequences for every part.
  */
 static int twin_tile_rows(int rows) { return rows <= 16 ? 16 : 64; }
@@ -195,7 +195,7 @@ int oracle_schedule(const int32_t* cache_seqlens, int batch, int rows, int num_p
                     int32_t* tile_metadata, int32_t* num_splits) {
   if (batch <= 0 || num_parts <= 0 || rows <= 0) return -1;
   const int tile = twin_tile_rows(rows);
-  const long long ovh = tile / 16 > 1 ? tile / 16 : 1;
+  const long long ovh = tile == 16 ? 3 : tile / 16;
   const long long qmin = 2 * ovh;
   long long* A = (long long*)malloc(sizeof(long long) * (size_t)batch);
   long long* B = (long long*)malloc(sizeof(long long) * (size_t)batch);

@@ -17,8 +17,10 @@ constexpr int kMaxBatch = 8192;
 // larger row counts the 64-row pair-split kernel (ceil(rows / 64) row tiles).
 __host__ __device__ constexpr int tile_rows_for(int rows) { return rows <= 16 ? 16 : 64; }
 // Fixed per-chunk cost, in page units, that the scheduler charges before each
-// sequence: loading the query tile and writing / re-reading a split partial.
-__host__ __device__ constexpr int sched_overhead(int tile) { return tile / 16 > 1 ? tile / 16 : 1; }
+// sequence: loading the query tile, the end-of-chunk merge and writing /
+// re-reading a split partial.  The 16-row token-split kernel's chunk end (a merge
+// of four waves' states through LDS) costs about three page loads.
+__host__ __device__ constexpr int sched_overhead(int tile) { return tile == 16 ? 3 : tile / 16; }
 __host__ __device__ constexpr int sched_min_part(int tile) { return 2 * sched_overhead(tile); }
 
 struct DecodeParams {

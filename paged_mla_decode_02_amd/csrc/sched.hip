@@ -9,8 +9,9 @@
 // The pages name the call only, so the partition below is this library's own:
 //
 //   work is measured in 64-token pages; sequence i costs m_i = max(ceil(L_i/64), 1)
-//   pages after a fixed overhead of OVH pages (query load, split partial), laid
-//   end to end: A_i = C_i + OVH, B_i = A_i + m_i, C_{i+1} = B_i, T = C_b.
+//   pages after a fixed overhead of OVH pages (query load, chunk-end merge,
+//   split partial), laid end to end: A_i = C_i + OVH, B_i = A_i + m_i,
+//   C_{i+1} = B_i, T = C_b.
 //   Parts are equal slices of q = max(ceil(T/P), QMIN) units of that line.
 //   Sequence i is split into part(B_i - 1) - part(A_i) + 1 chunks.
 //
