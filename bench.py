@@ -111,6 +111,78 @@ def cpu_baseline(w, bytes_step, target_s):
                       f"fp64, repeated {runs}x over {el:.1f} s; {per_run * 1e3:.1f} ms per pass"}
 
 
+def bench_absorb(args, torch, mla, workloads, dev):
+    """Time mla_absorb_q and mla_unabsorb_out for the workload's b*s_q tokens and
+    h_q heads: K graph-replayed steps (absorb + unabsorb), per-kernel HIP events."""
+    import numpy as np
+    cfg = workloads.CONFIGS[args.config]
+    b, s_q, h = cfg["batch"], cfg["s_q"], cfg["h_q"]
+    T = b * s_q
+    lay = workloads.make_layer_inputs(b, s_q, h, seed=args.config)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    qn, qr, wuk, wuv = up(lay.q_nope), up(lay.q_rope), up(lay.w_uk), up(lay.w_uv)
+    q_abs = torch.empty((b, s_q, h, 576), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.randn((b, s_q, h, 512), device=dev).to(torch.bfloat16)
+    out = torch.empty((b, s_q, h, 128), dtype=torch.bfloat16, device=dev)
+    # algorithmic bytes / flops of each GEMM: weights once, activations in and out
+    by_abs = 2 * (h * 128 * 512 + T * h * (128 + 64 + 576))
+    by_un = 2 * (h * 128 * 512 + T * h * (512 + 128))
+    fl = 2 * T * h * 128 * 512
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        mla.mla_absorb_q(qn, qr, wuk, out=q_abs)
+        if evs is not None:
+            evs[1].record()
+        mla.mla_unabsorb_out(o_lat, wuv, out=out)
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            step()
+    torch.cuda.current_stream().wait_stream(st)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    n_ev = min(K, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    torch.cuda._sleep(int(20e6))
+    for i in range(n_ev):
+        step(evs[i])
+    torch.cuda.synchronize()
+    d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs]).mean(axis=0)
+    gbs = [by_abs / (d[0] * 1e-3) / 1e9, by_un / (d[1] * 1e-3) / 1e9]
+    line = {
+        "metric": "MLA absorption GEMMs bf16 (q~ = W_UK^T q_nope, out = W_UV o_lat): achieved TB/s",
+        "value": round((by_abs + by_un) / (ms * 1e-3) / 1e12, 4), "unit": "TB/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg["name"], "tokens": T, "h_q": h, "d_nope": 128, "d_latent": 512, "d_v": 128},
+        "algorithmic": {"absorb_bytes": by_abs, "unabsorb_bytes": by_un, "flops_each": fl},
+        "kernel_ms": {"absorb": round(float(d[0]), 5), "unabsorb": round(float(d[1]), 5), "launches": n_ev},
+        "roofline": {"bound": "hbm", "achieved": round(gbs[0], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs[0] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "absorb_q",
+                     "unabsorb_achieved": round(gbs[1], 1), "unabsorb_frac": round(gbs[1] / HBM_PEAK_GBS, 4)},
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +192,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
+    ap.add_argument("--op", choices=["decode", "absorb"], default="decode",
+                    help="decode (default): the decode step; absorb: the two absorption GEMMs of the "
+                         "workload's query tokens and heads (one JSON line of their own)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -150,6 +225,9 @@ def main():
             b_.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
+    if args.op == "absorb":
+        bench_absorb(args, torch, mla, workloads, dev)
         return
     cfg = workloads.CONFIGS[args.config]
     w = workloads.config_workload(args.config)

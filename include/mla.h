@@ -160,6 +160,33 @@ int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message for the last non-zero status returned on this thread ("" if none). */
+/*
+ * The absorption GEMMs around the decode (per query head h; d_nope = d_v = 128,
+ * latent 512, rope 64).  The weight-absorption identity q.(W_UK c) = (W_UK^T q).c
+ * of the "FlashMLA inference acceleration" notes (dpshk.com/news/5996785, §2.1)
+ * lets every head score against the one cached latent row c; the value
+ * up-projection W_UV commutes with the softmax-weighted sum, so it is applied
+ * to the latent output afterwards.  Together with mla_decode_paged they form one
+ * MLA decode attention layer: absorb -> decode -> unabsorb.
+ *
+ * mla_absorb_q:  q_abs[t,h,0:512] = sum_n q_nope[t,h,n] * w_uk[h,n,0:512]
+ *                q_abs[t,h,512:576] = q_rope[t,h,0:64]
+ *   q_nope  bf16 [tokens, h_q, 128]   (tokens = batch * s_q, any order)
+ *   q_rope  bf16 [tokens, h_q, 64]
+ *   w_uk    bf16 [h_q, 128, 512]      (the nope key of head h is w_uk[h] . c)
+ *   q_abs   bf16 [tokens, h_q, 576]   out: the decode's q; fp32 accumulation,
+ *                                     rounded to bf16 (nearest even)
+ * mla_unabsorb_out:  out[t,h,v] = sum_c w_uv[h,v,c] * o_lat[t,h,c]
+ *   o_lat   bf16 [tokens, h_q, 512]   (the decode's out)
+ *   w_uv    bf16 [h_q, 128, 512]      (the value of head h is w_uv[h] . c)
+ *   out     bf16 [tokens, h_q, 128]   fp32 accumulation, rounded to bf16
+ * All pointers 16-byte aligned device pointers; tokens >= 0 (0 launches
+ * nothing and reads no pointer), h_q >= 1.  Errors: MLA_ERR_INVALID, MLA_ERR_HIP.
+ */
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int h_q, void* q_abs,
+                 void* stream);
+int mla_unabsorb_out(const void* o_lat, const void* w_uv, int tokens, int h_q, void* out, void* stream);
+
 const char* mla_last_error(void);
 
 #ifdef __cplusplus

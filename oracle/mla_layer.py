@@ -1,0 +1,97 @@
+"""CPU oracle for the MLA decode layer around the latent decode -- test
+infrastructure only (tests/, the smoke entry point and bench.py's CPU baseline
+may import it; the product library never does).  Plain numpy in fp64 on the
+exact bf16 input values; it shares no code with the HIP path.
+
+What it computes, per query head h (d_nope = d_v = 128, latent 512, rope 64):
+
+  absorb_q:      q~[t,h,0:512] = sum_n q_nope[t,h,n] W_UK[h,n,:],  q~[t,h,512:] = q_rope[t,h,:]
+  unabsorb_out:  out[t,h,v]    = sum_c W_UV[h,v,c] o_lat[t,h,c]
+  unabsorbed_attention: the MLA attention the two GEMMs and the latent decode
+      must reproduce, computed WITHOUT absorption: every head gets its own keys
+      k_t = [W_UK[h] c_t ; k_rope_t] and values v_t = W_UV[h] c_t from the cached
+      latent c_t = K_t[0:512] and rope key K_t[512:576], and
+      out = sum_t softmax(scale q.k)_t v_t over the visible keys (bottom-right
+      causal when s_q > 1), lse = ln sum_t exp(scale q.k_t).
+
+The absorption identity q.(W_UK c) = (W_UK^T q).c and the commuting of W_UV
+with the softmax-weighted sum are the "FlashMLA inference acceleration" notes
+(dpshk.com/news/5996785), §2.1; the unabsorbed form is the per-head attention
+those notes start from.  Matrix products use numpy's matmul as a library step.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+_PAGE = 64
+_LATENT = 512
+
+
+def _f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact)."""
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def absorb_q(q_nope_bits: np.ndarray, q_rope_bits: np.ndarray, w_uk_bits: np.ndarray) -> np.ndarray:
+    """q~ [..., h, 576] in fp64 from q_nope [..., h, 128], q_rope [..., h, 64], W_UK [h, 128, 512]."""
+    qn = _f64(q_nope_bits)
+    w = _f64(w_uk_bits)
+    lat = np.einsum("...hn,hnc->...hc", qn, w)
+    return np.concatenate([lat, _f64(q_rope_bits)], axis=-1)
+
+
+def unabsorb_out(o_lat: np.ndarray, w_uv_bits: np.ndarray) -> np.ndarray:
+    """out [..., h, 128] in fp64 from o_lat [..., h, 512] (fp64 values) and W_UV [h, 128, 512]."""
+    w = _f64(w_uv_bits)
+    return np.einsum("hvc,...hc->...hv", w, np.asarray(o_lat, dtype=np.float64))
+
+
+def unabsorbed_attention(w, layer, scale: Optional[float] = None,
+                         sel: Optional[Sequence[int]] = None):
+    """Reference MLA decode attention without absorption.
+
+    ``w`` is a workloads.Workload (paged latent cache, lengths, block table,
+    causal flag, h_kv must be 1); ``layer`` a workloads.LayerInputs.  Returns
+    (out [b, s_q, h_q, 128], lse [b, s_q, h_q]) in fp64, or, with ``sel`` (flat
+    indices (b * s_q + s) * h_q + h), the selected rows only as ([n, 128], [n])."""
+    if w.h_kv != 1:
+        raise ValueError("the layer reference covers one latent KV head")
+    scale = w.scale if scale is None else scale
+    qn = _f64(layer.q_nope)
+    qr = _f64(layer.q_rope)
+    w_uk = _f64(layer.w_uk)
+    w_uv = _f64(layer.w_uv)
+    b, s_q, h_q = w.batch, w.s_q, w.h_q
+    flat = range(b * s_q * h_q) if sel is None else list(sel)
+    outs, lses = [], []
+    cache = {}
+    for idx in flat:
+        bi, rem = divmod(int(idx), s_q * h_q)
+        s, h = divmod(rem, h_q)
+        L = int(w.cache_seqlens[bi])
+        n = L if not w.causal else max(0, L - s_q + s + 1)
+        if bi not in cache:
+            rows = [w.kcache[w.block_table[bi, t // _PAGE], t % _PAGE, 0] for t in range(L)]
+            cache[bi] = _f64(np.array(rows, dtype=np.uint16).reshape(L, -1)) if L else np.zeros((0, 576))
+        K = cache[bi][:n]
+        if n == 0:
+            outs.append(np.zeros(w_uv.shape[1]))
+            lses.append(-math.inf)
+            continue
+        c, k_rope = K[:, :_LATENT], K[:, _LATENT:]
+        k_nope = c @ w_uk[h].T          # per-head keys [n, 128]
+        v = c @ w_uv[h].T               # per-head values [n, 128]
+        x = scale * (k_nope @ qn[bi, s, h] + k_rope @ qr[bi, s, h])
+        m = x.max()
+        p = np.exp(x - m)
+        z = p.sum()
+        outs.append((p / z) @ v)
+        lses.append(m + math.log(z))
+    out = np.array(outs)
+    lse = np.array(lses)
+    if sel is None:
+        return out.reshape(b, s_q, h_q, -1), lse.reshape(b, s_q, h_q)
+    return out, lse

@@ -5,6 +5,9 @@ decode runs in the library's HIP kernels; this module only marshals torch
 tensors (device memory and the current stream) into the C ABI.  Importing it
 fails loudly when the library has not been built.
 
+The absorption GEMMs around the decode (same names as the C ABI):
+    mla_absorb_q(q_nope, q_rope, w_uk) -> q_abs      (the decode's query)
+    mla_unabsorb_out(o_lat, w_uv) -> out             (per-head values)
 Low-level calls, same names as the C ABI:
     mla_plan, mla_tile_rows, mla_get_metadata, mla_decode_paged,
     mla_decode_splitkv + mla_combine_splits (the two stages of mla_decode_paged)
@@ -26,6 +29,7 @@ import torch
 __all__ = [
     "LIB_PATH", "MlaError", "mla_plan", "mla_tile_rows", "mla_get_metadata", "mla_decode_paged",
     "mla_decode_splitkv", "mla_combine_splits", "get_mla_metadata", "flash_mla_with_kvcache",
+    "mla_absorb_q", "mla_unabsorb_out",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -58,6 +62,10 @@ def _load() -> ctypes.CDLL:
         fn.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
                        ctypes.c_float, P, P, P, SZ, P]
         fn.restype = I
+    lib.mla_absorb_q.argtypes = [P, P, P, I, I, P, P]
+    lib.mla_absorb_q.restype = I
+    lib.mla_unabsorb_out.argtypes = [P, P, I, I, P, P]
+    lib.mla_unabsorb_out.restype = I
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
     return lib
@@ -199,3 +207,56 @@ def flash_mla_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, block_table: 
         softmax_scale = q.shape[-1] ** -0.5
     return mla_decode_paged(q, k_cache, block_table, cache_seqlens, head_dim_v, tile_metadata,
                             num_splits, causal, softmax_scale)
+
+
+D_NOPE = 128
+D_ROPE = 64
+D_VHEAD = 128
+
+
+def _tokens_view(t: torch.Tensor, last: int, name: str):
+    """[..., h, last] -> (tokens, h) of a contiguous bf16 device tensor."""
+    _require(t, name, torch.bfloat16)
+    if t.dim() < 2 or t.shape[-1] != last:
+        raise ValueError(f"{name} must be [..., h, {last}]")
+    h = t.shape[-2]
+    return t.numel() // (h * last), h
+
+
+def mla_absorb_q(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """q_abs[..., h, 0:512] = W_UK[h]^T q_nope[..., h, :], q_abs[..., h, 512:] = q_rope.
+
+    q_nope [..., h_q, 128], q_rope [..., h_q, 64], w_uk [h_q, 128, 512] (bf16)."""
+    tokens, h_q = _tokens_view(q_nope, D_NOPE, "q_nope")
+    if _tokens_view(q_rope, D_ROPE, "q_rope") != (tokens, h_q) or q_rope.shape[:-1] != q_nope.shape[:-1]:
+        raise ValueError("q_rope must match q_nope's leading shape")
+    _require(w_uk, "w_uk", torch.bfloat16)
+    if tuple(w_uk.shape) != (h_q, D_NOPE, DV):
+        raise ValueError(f"w_uk must be [{h_q}, {D_NOPE}, {DV}]")
+    if out is None:
+        out = torch.empty(tuple(q_nope.shape[:-1]) + (D_QK,), dtype=torch.bfloat16, device=q_nope.device)
+    _require(out, "out", torch.bfloat16)
+    if out.shape[:-1] != q_nope.shape[:-1] or out.shape[-1] != D_QK:
+        raise ValueError("out must be [..., h_q, 576]")
+    _check(_lib.mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(), tokens, h_q,
+                             out.data_ptr(), _stream(q_nope.device)))
+    return out
+
+
+def mla_unabsorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[..., h, v] = sum_c W_UV[h, v, c] o_lat[..., h, c].
+
+    o_lat [..., h_q, 512] (the decode's output), w_uv [h_q, 128, 512] (bf16)."""
+    tokens, h_q = _tokens_view(o_lat, DV, "o_lat")
+    _require(w_uv, "w_uv", torch.bfloat16)
+    if tuple(w_uv.shape) != (h_q, D_VHEAD, DV):
+        raise ValueError(f"w_uv must be [{h_q}, {D_VHEAD}, {DV}]")
+    if out is None:
+        out = torch.empty(tuple(o_lat.shape[:-1]) + (D_VHEAD,), dtype=torch.bfloat16, device=o_lat.device)
+    _require(out, "out", torch.bfloat16)
+    if out.shape[:-1] != o_lat.shape[:-1] or out.shape[-1] != D_VHEAD:
+        raise ValueError("out must be [..., h_q, 128]")
+    _check(_lib.mla_unabsorb_out(o_lat.data_ptr(), w_uv.data_ptr(), tokens, h_q, out.data_ptr(),
+                                 _stream(o_lat.device)))
+    return out

@@ -206,3 +206,39 @@ int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages, con
 }
 
 }  // extern "C"
+
+namespace {
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+}  // namespace
+
+extern "C" {
+
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int tokens, int h_q, void* q_abs,
+                 void* stream) {
+  if (tokens < 0 || h_q <= 0)
+    return fail(MLA_ERR_INVALID, "tokens must be >= 0 and h_q > 0 (got %d, %d)", tokens, h_q);
+  if (tokens == 0) return ok();  // nothing to compute; the pointers are not used
+  if (!q_nope || !q_rope || !w_uk || !q_abs) return fail(MLA_ERR_INVALID, "null pointer");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(w_uk) || !aligned16(q_abs))
+    return fail(MLA_ERR_INVALID, "pointers must be 16-byte aligned");
+  hipError_t e = mla::launch_absorb_q(static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope),
+                                      static_cast<const uint16_t*>(w_uk), tokens, h_q, static_cast<uint16_t*>(q_abs),
+                                      (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "absorb launch");
+  return ok();
+}
+
+int mla_unabsorb_out(const void* o_lat, const void* w_uv, int tokens, int h_q, void* out, void* stream) {
+  if (tokens < 0 || h_q <= 0)
+    return fail(MLA_ERR_INVALID, "tokens must be >= 0 and h_q > 0 (got %d, %d)", tokens, h_q);
+  if (tokens == 0) return ok();  // nothing to compute; the pointers are not used
+  if (!o_lat || !w_uv || !out) return fail(MLA_ERR_INVALID, "null pointer");
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out))
+    return fail(MLA_ERR_INVALID, "pointers must be 16-byte aligned");
+  hipError_t e = mla::launch_unabsorb_out(static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(w_uv),
+                                          tokens, h_q, static_cast<uint16_t*>(out), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "unabsorb launch");
+  return ok();
+}
+
+}  // extern "C"

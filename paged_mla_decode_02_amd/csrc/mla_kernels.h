@@ -11,6 +11,11 @@ constexpr int kDqk = 576;          // latent 512 + rope 64
 constexpr int kDv = 512;           // value width (latent part of each row)
 constexpr int kRowBytes = kDqk * 2;
 constexpr int kMdInts = 8;
+// MLA head geometry around the latent decode (absorption GEMMs)
+constexpr int kNope = 128;         // non-rope query/key dims per head
+constexpr int kRope = 64;          // rope dims (kDqk = kLatent + kRope)
+constexpr int kLatent = 512;       // compressed latent width (= kDv)
+constexpr int kDvOut = 128;        // value dims per head after W_UV
 constexpr int kMaxBatch = 8192;
 
 // Query rows one workgroup owns: <= 16 rows use the 16-row token-split kernel,
@@ -44,5 +49,9 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int rows, int num_
                            int32_t* tile_md, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int tokens,
+                           int h_q, uint16_t* q_abs, hipStream_t stream);
+hipError_t launch_unabsorb_out(const uint16_t* o_lat, const uint16_t* w_uv, int tokens, int h_q, uint16_t* out,
+                               hipStream_t stream);
 
 }  // namespace mla

@@ -123,3 +123,22 @@ def test_python_binding_imports():
     assert mla.mla_plan(64, 16, 1, 512, 256) == (256, (64 + 256) * 16 * 513 * 4)
     with pytest.raises(mla.MlaError):
         mla.mla_plan(0, 16, 1, 512, 256)
+
+
+def test_absorb_calls_reject(lib):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.mla_absorb_q.argtypes = [P, P, P, I, I, P, P]
+    lib.mla_unabsorb_out.argtypes = [P, P, I, I, P, P]
+    assert lib.mla_absorb_q(None, FAKE, FAKE, 4, 16, FAKE, None) == MLA_ERR_INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, -1, 16, FAKE, None) == MLA_ERR_INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 4, 0, FAKE, None) == MLA_ERR_INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE + 2, FAKE, 4, 16, FAKE, None) == MLA_ERR_INVALID
+    assert lib.mla_absorb_q(FAKE, FAKE, FAKE, 0, 16, FAKE, None) == MLA_OK  # nothing to do, no launch
+    assert lib.mla_unabsorb_out(FAKE, None, 4, 16, FAKE, None) == MLA_ERR_INVALID
+    assert lib.mla_unabsorb_out(FAKE, FAKE, 4, -3, FAKE, None) == MLA_ERR_INVALID
+    assert lib.mla_unabsorb_out(FAKE, FAKE, 4, 16, FAKE + 8, None) == MLA_ERR_INVALID
+    assert lib.mla_unabsorb_out(FAKE, FAKE, 4, 16, FAKE + 8, None) == MLA_ERR_INVALID
+    assert lib.mla_last_error()
+    assert lib.mla_unabsorb_out(FAKE, FAKE, 0, 16, FAKE, None) == MLA_OK
+    assert lib.mla_unabsorb_out(None, None, 0, 16, None, None) == MLA_OK  # no tokens: pointers unused
+    assert lib.mla_absorb_q(None, None, None, 0, 16, None, None) == MLA_OK

@@ -1,0 +1,96 @@
+"""Pins of the MLA layer oracle (oracle/mla_layer.py) against what the pages and
+the mathematics fix, independently of its own formulas:
+
+* the absorption GEMM and the up-projection against explicit loops on a few
+  heads and tokens (a transposed or mis-indexed weight fails);
+* a closed form: W_UK[h] = [I_128 | 0] makes the absorbed latent query the
+  nope query followed by zeros;
+* the layer identity of the "FlashMLA inference acceleration" notes
+  (dpshk.com/news/5996785), §2.1: absorb -> latent decode (the C oracle) ->
+  up-projection equals per-head attention with up-projected keys and values.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import mla_layer
+from workloads import bf16_bits, make_layer_inputs, make_workload
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def f64(bits):
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def test_absorb_against_loops():
+    lay = make_layer_inputs(1, 3, 2, seed=11)
+    got = mla_layer.absorb_q(lay.q_nope, lay.q_rope, lay.w_uk)
+    qn, qr, w = f64(lay.q_nope), f64(lay.q_rope), f64(lay.w_uk)
+    for s in range(3):
+        for h in range(2):
+            for c in range(0, 512, 37):
+                acc = 0.0
+                for n in range(128):
+                    acc += qn[0, s, h, n] * w[h, n, c]
+                assert abs(got[0, s, h, c] - acc) < 1e-12 * (1 + abs(acc))
+            for r in range(64):
+                assert got[0, s, h, 512 + r] == qr[0, s, h, r]
+
+
+def test_unabsorb_against_loops():
+    lay = make_layer_inputs(1, 2, 2, seed=12)
+    rng = np.random.default_rng(3)
+    o = rng.standard_normal((1, 2, 2, 512))
+    got = mla_layer.unabsorb_out(o, lay.w_uv)
+    w = f64(lay.w_uv)
+    for s in range(2):
+        for h in range(2):
+            for v in range(0, 128, 9):
+                acc = 0.0
+                for c in range(512):
+                    acc += w[h, v, c] * o[0, s, h, c]
+                assert abs(got[0, s, h, v] - acc) < 1e-12 * (1 + abs(acc))
+
+
+def test_absorb_identity_weight_closed_form():
+    lay = make_layer_inputs(2, 1, 3, seed=13)
+    eye = np.zeros((3, 128, 512), dtype=np.float32)
+    for h in range(3):
+        eye[h, :, :128] = np.eye(128, dtype=np.float32)
+    got = mla_layer.absorb_q(lay.q_nope, lay.q_rope, bf16_bits(eye))
+    assert np.array_equal(got[..., :128], f64(lay.q_nope))
+    assert not np.any(got[..., 128:512])
+
+
+@pytest.mark.parametrize("causal,s_q", [(False, 1), (True, 2)])
+def test_layer_identity(oracle_lib, causal, s_q):
+    """absorb -> latent decode -> up-projection == unabsorbed attention.
+
+    W_UK and q_nope are small integers so that the absorbed query is exact in
+    bf16 and the two sides agree to rounding of fp64 sums."""
+    rng = np.random.default_rng(21)
+    H, lens = 4, [130, 64, 1]
+    w = make_workload(lens, s_q=s_q, h_q=H, causal=causal, seed=5)
+    lay = make_layer_inputs(len(lens), s_q, H, seed=6)
+    lay.q_nope = bf16_bits(rng.integers(-1, 2, size=lay.q_nope.shape).astype(np.float32))
+    lay.w_uk = bf16_bits(rng.integers(-1, 2, size=lay.w_uk.shape).astype(np.float32))
+    q_abs = mla_layer.absorb_q(lay.q_nope, lay.q_rope, lay.w_uk)
+    qb = bf16_bits(q_abs.astype(np.float32))
+    assert np.array_equal(f64(qb), q_abs), "absorbed query must be exact in bf16 here"
+    w.q = qb
+    o_lat, lse_lat = oracle_lib.decode(w)
+    o_lat = o_lat.reshape(w.batch, s_q, H, 512)
+    lse_lat = lse_lat.reshape(w.batch, s_q, H)
+    out = mla_layer.unabsorb_out(o_lat, lay.w_uv)
+    ref_out, ref_lse = mla_layer.unabsorbed_attention(w, lay)
+    np.testing.assert_allclose(out, ref_out, rtol=1e-10, atol=1e-10)
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(fin, np.isfinite(lse_lat))
+    np.testing.assert_allclose(lse_lat[fin], ref_lse[fin], rtol=0, atol=1e-10)
+    # sampled rows agree with the full evaluation
+    sel = [0, 5, w.batch * s_q * H - 1]
+    so, sl = mla_layer.unabsorbed_attention(w, lay, sel=sel)
+    np.testing.assert_allclose(so, ref_out.reshape(-1, 128)[sel], rtol=0, atol=0)
+    assert math.isclose(sl[0], ref_lse.reshape(-1)[0], rel_tol=0, abs_tol=0)

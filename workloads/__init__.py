@@ -197,3 +197,31 @@ def permute_pages(w: Workload, seed: int) -> Workload:
     m = bt >= 0
     bt[m] = perm[bt[m]]
     return dataclasses.replace(w, kcache=kc, block_table=bt)
+
+
+D_NOPE = 128
+D_ROPE = 64
+D_VHEAD = 128
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """Per-head query parts and up-projection weights of one MLA decode layer
+    (bf16 bits): the absorbed query of the decode is built from these."""
+    q_nope: np.ndarray  # [b, s_q, h_q, 128]
+    q_rope: np.ndarray  # [b, s_q, h_q, 64]
+    w_uk: np.ndarray    # [h_q, 128, 512]: the nope key of head h is w_uk[h] . c
+    w_uv: np.ndarray    # [h_q, 128, 512]: the value of head h is w_uv[h] . c
+
+
+def make_layer_inputs(batch: int, s_q: int, h_q: int, seed: int) -> LayerInputs:
+    """Seeded draws, in this order: q_nope ~ N(0,1), q_rope ~ N(0,1),
+    w_uk ~ N(0, 1/512), w_uv ~ N(0, 1/512) (fan-in of the 512-wide latent), each
+    rounded to bf16 (nearest even)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q_nope = bf16_bits(rng.standard_normal((batch, s_q, h_q, D_NOPE), dtype=np.float32))
+    q_rope = bf16_bits(rng.standard_normal((batch, s_q, h_q, D_ROPE), dtype=np.float32))
+    s = np.float32(1.0 / math.sqrt(DV))
+    w_uk = bf16_bits(rng.standard_normal((h_q, D_NOPE, DV), dtype=np.float32) * s)
+    w_uv = bf16_bits(rng.standard_normal((h_q, D_VHEAD, DV), dtype=np.float32) * s)
+    return LayerInputs(q_nope=q_nope, q_rope=q_rope, w_uk=w_uk, w_uv=w_uv)
