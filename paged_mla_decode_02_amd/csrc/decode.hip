@@ -93,6 +93,13 @@ __device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Wait for every vector-memory operation, visibly to the compiler (vmcnt(0)).
+// The compiler counts only the loads it issued itself; a wait it places before
+// the first use of such a load would also cover every page transfer issued
+// since, so loads whose results are used across page transfers (queries, page
+// ids, lengths of the next sequence) are drained here, at points where nothing
+// else is in flight that the kernel does not need at once anyway.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ float wave_max16(float v) {  // max over lanes l, l^16, l^32, l^48
   v = fmaxf(v, __shfl_xor(v, 16, 64));
@@ -145,10 +152,23 @@ struct SeqRange {
   bool ok;
 };
 
-__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b, int i0, int f0, int j0,
-                                              int e0, int ord0) {
+// A sequence's length and workspace slots, read with scalar loads (constant
+// address space): they are waited for through lgkmcnt, never through vmcnt, so
+// they can be fetched ahead without tying a wait to the page transfers.
+#define CONST_AS __attribute__((address_space(4)))
+struct SeqDesc {
+  int L, base, next;  // cache_seqlens[b], num_splits[b], num_splits[b + 1]
+};
+__device__ __forceinline__ SeqDesc load_seq(const DecodeParams& p, int b) {
+  const CONST_AS int32_t* sl = (const CONST_AS int32_t*)p.seqlens;
+  const CONST_AS int32_t* ns = (const CONST_AS int32_t*)p.num_splits;
+  return SeqDesc{sl[b], ns[b], ns[b + 1]};
+}
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, const SeqDesc& d, int b, int i0, int f0,
+                                              int j0, int e0, int ord0) {
   SeqRange r;
-  r.L = p.seqlens[b];
+  r.L = d.L;
   if (r.L < 0) r.L = 0;
   r.nb = (r.L + kPage - 1) / kPage;
   r.lo = (b == i0) ? f0 : 0;
@@ -157,13 +177,17 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b, int 
   if (r.lo < 0) r.lo = 0;
   if (r.lo > r.hi) r.lo = r.hi;
   r.ord = (b == i0) ? ord0 : 0;
-  r.base = p.num_splits[b];
-  r.chunks = p.num_splits[b + 1] - r.base;
+  r.base = d.base;
+  r.chunks = d.next - r.base;
   // metadata that does not belong to these lengths / part count must not make
   // the epilogue write outside the workspace: such a chunk writes nothing
   const long long slot = (long long)r.base + r.ord;
   r.ok = r.ord >= 0 && r.ord < r.chunks && slot >= 0 && slot < (long long)p.batch + p.num_parts;
   return r;
+}
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b, int i0, int f0, int j0, int e0,
+                                              int ord0) {
+  return seq_range(p, load_seq(p, b), b, i0, f0, j0, e0, ord0);
 }
 
 // Block-table entries of pages [base, base + 64) of sequence b, one per lane
@@ -307,21 +331,35 @@ decode_tokensplit(DecodeParams p) {
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = qp[ks * 4];
   };
 
-  // in-flight DMA only ever targets buffer `buf`; buf ^ 1 is free between pages
+  // in-flight DMA only ever targets buffer `buf`; buf ^ 1 is free between pages.
+  // Sequence descriptors (lengths, page ids) are loaded two sequences ahead and
+  // queries one ahead, so each is complete at the drain that ends the epilogue
+  // before the one that uses it.
   int buf = 0;
   int b = i0;
-  int ids = load_page_ids(p, b, b == i0 ? f0 : 0, lane);
+  int ids = load_page_ids(p, b, f0, lane);
   SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
-  if (sr.lo != f0) ids = load_page_ids(p, b, sr.lo, lane);  // clamped (malformed) metadata
   load_q(b);
+  SeqDesc nd = {};
+  int nids = -1;
+  if (b < j0) {
+    nids = load_page_ids(p, b + 1, 0, lane);
+    nd = load_seq(p, b + 1);
+  }
+  vm_drain();
+  SeqRange nr = seq_range(p, nd, b + 1, i0, f0, j0, e0, ord0);
+  if (sr.lo != f0) {  // clamped (malformed) metadata
+    ids = load_page_ids(p, b, sr.lo, lane);
+    vm_drain();
+  }
   if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
   for (;;) {
     const bool has_next = b < j0;
-    SeqRange nr = {};
-    int nids = -1;
-    if (has_next) {
-      nids = load_page_ids(p, b + 1, 0, lane);
-      nr = seq_range(p, b + 1, i0, f0, j0, e0, ord0);
+    SeqDesc nd2 = {};
+    int nids2 = -1;
+    if (b + 1 < j0) {
+      nids2 = load_page_ids(p, b + 2, 0, lane);
+      nd2 = load_seq(p, b + 2);
     }
     int s;
     long long qo;
@@ -510,11 +548,14 @@ decode_tokensplit(DecodeParams p) {
       else p.lse[ro] = l2 * kLn2;
     }
     if (!has_next) break;
+    vm_drain();  // the next queries and descriptors (and this epilogue's stores)
     // advance the stream; an empty sequence requested nothing, so its successor
     // starts its own first page now (buffer `buf`, idle)
     ++b;
     sr = nr;
     ids = nids;
+    nr = seq_range(p, nd2, b + 1, i0, f0, j0, e0, ord0);
+    nids = nids2;
     if (!next_started && sr.lo < sr.hi) dma_slice(slices + buf * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
   }
 }
