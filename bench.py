@@ -183,6 +183,70 @@ def bench_absorb(args, torch, mla, workloads, dev):
     print(json.dumps(line))
 
 
+def bench_append(args, torch, mla, workloads, dev):
+    """Time mla_kv_append for one decode step of the workload: every sequence
+    appends s_q new cache rows after its current length (graph-replayed steps,
+    per-launch HIP events)."""
+    import numpy as np
+    cfg = workloads.CONFIGS[args.config]
+    w0 = workloads.config_workload(args.config)
+    s_new = args.append_tokens or cfg["s_q"]
+    w, before, new_kv = workloads.make_append_case(w0.cache_seqlens, s_new, h_q=w0.h_q, seed=args.config)
+    del w0
+    kc = torch.from_numpy(w.kcache.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(before).to(dev)
+    nk = torch.from_numpy(new_kv.view(np.int16)).to(dev).view(torch.bfloat16)
+    nl = torch.empty_like(sl)
+    rows = w.batch * s_new * w.h_kv
+    by = 2 * rows * 576 * 2 + 4 * w.batch * 2 + 4 * w.batch * ((s_new + 63) // 64 + 1)
+
+    def step():
+        mla.mla_kv_append(nk, sl, bt, kc, new_seqlens=nl)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            step()
+    torch.cuda.current_stream().wait_stream(st)
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    n_ev = min(K, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    torch.cuda._sleep(int(20e6))
+    for i in range(n_ev):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    d = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gbs = by / (d * 1e-3) / 1e9
+    line = {
+        "metric": "paged KV append bf16 (new latent+rope rows scattered into 64-token pages): achieved TB/s",
+        "value": round(by / (ms * 1e-3) / 1e12, 4), "unit": "TB/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg["name"], "batch": w.batch, "s_new": s_new, "h_kv": w.h_kv, "rows": rows},
+        "algorithmic": {"bytes_per_step": by},
+        "kernel_ms": {"append": round(d, 5), "launches": n_ev},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "kv_append"},
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,7 +256,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
-    ap.add_argument("--op", choices=["decode", "absorb"], default="decode",
+    ap.add_argument("--append-tokens", type=int, default=0,
+                    help="--op append: rows appended per sequence (default: the workload's s_q)")
+    ap.add_argument("--op", choices=["decode", "absorb", "append"], default="decode",
                     help="decode (default): the decode step; absorb: the two absorption GEMMs of the "
                          "workload's query tokens and heads (one JSON line of their own)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -228,6 +294,9 @@ def main():
         return
     if args.op == "absorb":
         bench_absorb(args, torch, mla, workloads, dev)
+        return
+    if args.op == "append":
+        bench_append(args, torch, mla, workloads, dev)
         return
     cfg = workloads.CONFIGS[args.config]
     w = workloads.config_workload(args.config)

@@ -59,6 +59,7 @@ extern "C" {
 #define MLA_ERR_UNSUPPORTED (-2) /* d_qk != 576, dv != 512, page size != 64, batch above MLA_MAX_BATCH */
 #define MLA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than mla_plan's size */
 #define MLA_ERR_HIP (-4)         /* a HIP runtime call failed; see mla_last_error() */
+#define MLA_ERR_CAPACITY (-5)    /* page allocator: no free page, or more pages than max_blocks */
 
 #define MLA_PAGE_BLOCK_SIZE 64
 #define MLA_D_QK 576
@@ -159,7 +160,6 @@ int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages,
                        int causal, float softmax_scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Message for the last non-zero status returned on this thread ("" if none). */
 /*
  * The absorption GEMMs around the decode (per query head h; d_nope = d_v = 128,
  * latent 512, rope 64).  The weight-absorption identity q.(W_UK c) = (W_UK^T q).c
@@ -187,6 +187,71 @@ int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int t
                  void* stream);
 int mla_unabsorb_out(const void* o_lat, const void* w_uv, int tokens, int h_q, void* out, void* stream);
 
+/*
+ * Paged KV cache: appending the newest tokens' rows and allocating pages.  The
+ * "Flash MLA: efficient MLA decoding kernel library for variable-length
+ * sequences" page (developer.baidu.com, §三.1; §四 steps 2 and 5) keeps the
+ * cache in fixed-size pages reached through two levels of page tables -- one
+ * per sequence, one over the physical pages -- gives a sequence of n tokens
+ * ceil(n / page_size) pages, takes pages as it grows and returns them when it
+ * ends.  The page size is 64 tokens (the pages' 4096 in that listing is read
+ * as the 64 of the kernel's page table).
+ *
+ * mla_kv_append: for b < batch, j < s_new, k < h_kv, with L = cache_seqlens[b]
+ * (the length BEFORE the append; negative counts as 0) and t = L + j:
+ *   kcache[block_table[b][t / 64], t % 64, k, :] = new_kv[b, j, k, :]
+ * and, when new_seqlens is not NULL, new_seqlens[b] = L + s_new.
+ *   new_kv       bf16 [batch, s_new, h_kv, 576] device, 16-byte aligned
+ *   cache_seqlens int32 [batch] device
+ *   block_table  int32 [batch, max_blocks] device; the entries that cover the
+ *                new positions must already hold pages (mla_pager_reserve);
+ *                a row whose page id is negative, >= num_pages or past
+ *                max_blocks is not written (no fault, nothing reported)
+ *   kcache       bf16 [num_pages, 64, h_kv, 576] device, 16-byte aligned, in/out
+ *   new_seqlens  int32 [batch] device or NULL; must not alias cache_seqlens
+ * batch == 0 launches nothing and reads no pointer.  Rows of different (b, j)
+ * must map to different slots (distinct sequences own distinct pages), else
+ * which write wins is unspecified.
+ * Errors: MLA_ERR_INVALID, MLA_ERR_UNSUPPORTED (more than 2^31 / 72 rows), MLA_ERR_HIP.
+ */
+int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
+                  const int32_t* block_table, int max_blocks, void* kcache, int64_t num_pages,
+                  int32_t* new_seqlens, void* stream);
+
+/*
+ * Host page allocator (no GPU call).  Its whole state -- the free-page stack,
+ * the owner of every physical page and the per-sequence page tables, which are
+ * the rows of a host block table [max_seqs, max_blocks] int32 (-1 = no page) --
+ * lives in one caller-owned host buffer of mla_pager_bytes() bytes (4-byte
+ * aligned).  Not thread-safe: calls on one state must be serialised.
+ *   mla_pager_bytes      state size, 0 if a size is not positive
+ *   mla_pager_init       empty pool of num_pages pages, every table row -1
+ *   mla_pager_reserve    grow sequence seq to hold new_len tokens: it gets
+ *                        ceil(new_len / 64) pages, the new ones appended to its
+ *                        row; a shorter new_len changes nothing.  On
+ *                        MLA_ERR_CAPACITY (pool empty, or more than max_blocks
+ *                        pages) the state is unchanged.
+ *   mla_pager_release    return all pages of seq to the pool; its row becomes -1
+ *   mla_pager_free_pages number of free pages (or a negative status)
+ *   mla_pager_seq_pages  pages held by seq (or a negative status)
+ *   mla_pager_page_owner sequence holding a page, -1 if free (or a negative status)
+ *   mla_pager_block_table pointer to the host block table inside the state
+ *                        (NULL if not initialised); copy it to the device for
+ *                        mla_kv_append / mla_decode_paged
+ * Policy: free pages form a stack (fresh pool: ascending ids; released pages
+ * are taken again first).  Errors: MLA_ERR_INVALID, MLA_ERR_WORKSPACE (buffer
+ * too small), MLA_ERR_CAPACITY.
+ */
+size_t mla_pager_bytes(int num_pages, int max_seqs, int max_blocks);
+int mla_pager_init(void* state, size_t bytes, int num_pages, int max_seqs, int max_blocks);
+int mla_pager_reserve(void* state, int seq, int64_t new_len);
+int mla_pager_release(void* state, int seq);
+int mla_pager_free_pages(const void* state);
+int mla_pager_seq_pages(const void* state, int seq);
+int mla_pager_page_owner(const void* state, int page);
+const int32_t* mla_pager_block_table(const void* state);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
 const char* mla_last_error(void);
 
 #ifdef __cplusplus

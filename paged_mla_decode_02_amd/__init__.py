@@ -5,6 +5,10 @@ decode runs in the library's HIP kernels; this module only marshals torch
 tensors (device memory and the current stream) into the C ABI.  Importing it
 fails loudly when the library has not been built.
 
+The paged cache (same names as the C ABI):
+    mla_kv_append(new_kv, cache_seqlens, block_table, kcache) -> new_seqlens
+    Pager(num_pages, max_seqs, max_blocks): host page allocator (reserve,
+        release, block_table)
 The absorption GEMMs around the decode (same names as the C ABI):
     mla_absorb_q(q_nope, q_rope, w_uk) -> q_abs      (the decode's query)
     mla_unabsorb_out(o_lat, w_uv) -> out             (per-head values)
@@ -29,7 +33,7 @@ import torch
 __all__ = [
     "LIB_PATH", "MlaError", "mla_plan", "mla_tile_rows", "mla_get_metadata", "mla_decode_paged",
     "mla_decode_splitkv", "mla_combine_splits", "get_mla_metadata", "flash_mla_with_kvcache",
-    "mla_absorb_q", "mla_unabsorb_out",
+    "mla_absorb_q", "mla_unabsorb_out", "mla_kv_append", "Pager",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -66,6 +70,24 @@ def _load() -> ctypes.CDLL:
     lib.mla_absorb_q.restype = I
     lib.mla_unabsorb_out.argtypes = [P, P, I, I, P, P]
     lib.mla_unabsorb_out.restype = I
+    lib.mla_kv_append.argtypes = [P, I, I, I, P, P, I, P, ctypes.c_int64, P, P]
+    lib.mla_kv_append.restype = I
+    lib.mla_pager_bytes.argtypes = [I, I, I]
+    lib.mla_pager_bytes.restype = SZ
+    lib.mla_pager_init.argtypes = [P, SZ, I, I, I]
+    lib.mla_pager_init.restype = I
+    lib.mla_pager_reserve.argtypes = [P, I, ctypes.c_int64]
+    lib.mla_pager_reserve.restype = I
+    lib.mla_pager_release.argtypes = [P, I]
+    lib.mla_pager_release.restype = I
+    for name in ("mla_pager_free_pages",):
+        getattr(lib, name).argtypes = [P]
+        getattr(lib, name).restype = I
+    for name in ("mla_pager_seq_pages", "mla_pager_page_owner"):
+        getattr(lib, name).argtypes = [P, I]
+        getattr(lib, name).restype = I
+    lib.mla_pager_block_table.argtypes = [P]
+    lib.mla_pager_block_table.restype = ctypes.POINTER(ctypes.c_int32)
     lib.mla_last_error.argtypes = []
     lib.mla_last_error.restype = ctypes.c_char_p
     return lib
@@ -260,3 +282,73 @@ def mla_unabsorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torc
     _check(_lib.mla_unabsorb_out(o_lat.data_ptr(), w_uv.data_ptr(), tokens, h_q, out.data_ptr(),
                                  _stream(o_lat.device)))
     return out
+
+
+def mla_kv_append(new_kv: torch.Tensor, cache_seqlens: torch.Tensor, block_table: torch.Tensor,
+                  kcache: torch.Tensor, new_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Write new_kv [b, s_new, h_kv, 576] at positions cache_seqlens[b] + j of
+    each sequence's pages (in place in kcache); returns cache_seqlens + s_new."""
+    _require(new_kv, "new_kv", torch.bfloat16)
+    _require(kcache, "kcache", torch.bfloat16)
+    _require(cache_seqlens, "cache_seqlens", torch.int32)
+    _require(block_table, "block_table", torch.int32)
+    if new_kv.dim() != 4 or new_kv.shape[-1] != D_QK:
+        raise ValueError("new_kv must be [batch, s_new, h_kv, 576]")
+    b, s_new, h_kv, _ = new_kv.shape
+    if kcache.dim() != 4 or kcache.shape[1] != PAGE_BLOCK_SIZE or kcache.shape[2] != h_kv or kcache.shape[3] != D_QK:
+        raise ValueError(f"kcache must be [num_pages, 64, {h_kv}, 576]")
+    if cache_seqlens.shape != (b,) or block_table.dim() != 2 or block_table.shape[0] != b:
+        raise ValueError("cache_seqlens must be [batch] and block_table [batch, max_blocks]")
+    if new_seqlens is None:
+        new_seqlens = torch.empty_like(cache_seqlens)
+    _require(new_seqlens, "new_seqlens", torch.int32)
+    _check(_lib.mla_kv_append(new_kv.data_ptr(), b, s_new, h_kv, cache_seqlens.data_ptr(), block_table.data_ptr(),
+                              block_table.shape[1], kcache.data_ptr(), kcache.shape[0], new_seqlens.data_ptr(),
+                              _stream(kcache.device)))
+    return new_seqlens
+
+
+class Pager:
+    """Host page allocator of the paged cache (mla_pager_* of the C ABI).
+
+    Its state, including the block table [max_seqs, max_blocks] int32 (-1 = no
+    page), lives in a host buffer owned by this object."""
+
+    def __init__(self, num_pages: int, max_seqs: int, max_blocks: int):
+        n = _lib.mla_pager_bytes(num_pages, max_seqs, max_blocks)
+        if n == 0:
+            raise ValueError("num_pages, max_seqs and max_blocks must be positive")
+        self._buf = (ctypes.c_int32 * ((n + 3) // 4))()
+        self._ptr = ctypes.addressof(self._buf)
+        _check(_lib.mla_pager_init(self._ptr, n, num_pages, max_seqs, max_blocks))
+        self.num_pages, self.max_seqs, self.max_blocks = num_pages, max_seqs, max_blocks
+
+    def reserve(self, seq: int, new_len: int) -> None:
+        """Make sequence seq hold new_len tokens (ceil(new_len / 64) pages)."""
+        _check(_lib.mla_pager_reserve(self._ptr, seq, new_len))
+
+    def release(self, seq: int) -> None:
+        _check(_lib.mla_pager_release(self._ptr, seq))
+
+    def free_pages(self) -> int:
+        r = _lib.mla_pager_free_pages(self._ptr)
+        _check(min(r, 0))
+        return r
+
+    def seq_pages(self, seq: int) -> int:
+        r = _lib.mla_pager_seq_pages(self._ptr, seq)
+        _check(min(r, 0))
+        return r
+
+    def page_owner(self, page: int) -> int:
+        r = _lib.mla_pager_page_owner(self._ptr, page)
+        if r < -1:
+            _check(r)
+        return r
+
+    def block_table(self) -> torch.Tensor:
+        """A CPU copy of the block table [max_seqs, max_blocks] int32."""
+        p = _lib.mla_pager_block_table(self._ptr)
+        n = self.max_seqs * self.max_blocks
+        arr = (ctypes.c_int32 * n).from_address(ctypes.addressof(p.contents))
+        return torch.frombuffer(bytearray(arr), dtype=torch.int32).reshape(self.max_seqs, self.max_blocks)

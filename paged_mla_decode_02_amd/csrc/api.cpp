@@ -27,6 +27,15 @@ int ok() {
   return MLA_OK;
 }
 
+}  // namespace
+
+int mla::set_status(int code, const char* msg) {
+  std::snprintf(g_err, sizeof g_err, "%s", code == MLA_OK ? "" : msg);
+  return code;
+}
+
+namespace {
+
 int hip_fail(hipError_t e, const char* what) {
   return fail(MLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -238,6 +247,32 @@ int mla_unabsorb_out(const void* o_lat, const void* w_uv, int tokens, int h_q, v
   hipError_t e = mla::launch_unabsorb_out(static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(w_uv),
                                           tokens, h_q, static_cast<uint16_t*>(out), (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "unabsorb launch");
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
+                  const int32_t* block_table, int max_blocks, void* kcache, int64_t num_pages,
+                  int32_t* new_seqlens, void* stream) {
+  if (batch < 0 || s_new < 0) return fail(MLA_ERR_INVALID, "batch and s_new must be >= 0 (got %d, %d)", batch, s_new);
+  if (batch == 0) return ok();  // nothing to write; the pointers are not used
+  if (h_kv <= 0 || max_blocks <= 0 || num_pages <= 0)
+    return fail(MLA_ERR_INVALID, "h_kv, max_blocks and num_pages must be positive");
+  if (!cache_seqlens || !block_table || !kcache || (s_new > 0 && !new_kv))
+    return fail(MLA_ERR_INVALID, "null pointer");
+  if (new_seqlens && new_seqlens == cache_seqlens)
+    return fail(MLA_ERR_INVALID, "new_seqlens must not alias cache_seqlens");
+  if ((s_new > 0 && !aligned16(new_kv)) || !aligned16(kcache))
+    return fail(MLA_ERR_INVALID, "new_kv and kcache must be 16-byte aligned");
+  if ((long long)batch * s_new * h_kv * (MLA_D_QK * 2 / 16) >= (1LL << 31))
+    return fail(MLA_ERR_UNSUPPORTED, "batch * s_new * h_kv too large for one call");
+  hipError_t e = mla::launch_kv_append(static_cast<const uint16_t*>(new_kv), batch, s_new, h_kv, cache_seqlens,
+                                       block_table, max_blocks, static_cast<uint16_t*>(kcache), num_pages,
+                                       new_seqlens, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "kv append launch");
   return ok();
 }
 

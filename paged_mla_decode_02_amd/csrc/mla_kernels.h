@@ -45,12 +45,19 @@ struct DecodeParams {
   int xcd_map;               // workgroup -> (part, row tile, kv head) mapping keeps a part on one XCD
 };
 
+// Records the status of the last C-ABI call on this thread (message for
+// mla_last_error) and returns `code`.
+int set_status(int code, const char* msg);
+
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int rows, int num_parts,
                            int32_t* tile_md, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int tokens,
                            int h_q, uint16_t* q_abs, hipStream_t stream);
+hipError_t launch_kv_append(const uint16_t* new_kv, int batch, int s_new, int h_kv, const int32_t* seqlens,
+                            const int32_t* block_table, int max_blocks, uint16_t* kcache, long long num_pages,
+                            int32_t* new_seqlens, hipStream_t stream);
 hipError_t launch_unabsorb_out(const uint16_t* o_lat, const uint16_t* w_uv, int tokens, int h_q, uint16_t* out,
                                hipStream_t stream);
 

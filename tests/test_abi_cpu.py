@@ -142,3 +142,31 @@ def test_absorb_calls_reject(lib):
     assert lib.mla_unabsorb_out(FAKE, FAKE, 0, 16, FAKE, None) == MLA_OK
     assert lib.mla_unabsorb_out(None, None, 0, 16, None, None) == MLA_OK  # no tokens: pointers unused
     assert lib.mla_absorb_q(None, None, None, 0, 16, None, None) == MLA_OK
+
+
+def test_kv_append_rejects(lib):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.mla_kv_append.argtypes = [P, I, I, I, P, P, I, P, ctypes.c_int64, P, P]
+    good = dict(new_kv=FAKE, batch=4, s_new=1, h_kv=1, lens=FAKE + 64, bt=FAKE + 128, max_blocks=8, kc=FAKE,
+                num_pages=10, new_lens=FAKE + 256)
+
+    def call(**over):
+        a = dict(good, **over)
+        return lib.mla_kv_append(a["new_kv"], a["batch"], a["s_new"], a["h_kv"], a["lens"], a["bt"],
+                                 a["max_blocks"], a["kc"], a["num_pages"], a["new_lens"], None)
+
+    assert call(batch=-1) == MLA_ERR_INVALID
+    assert call(s_new=-2) == MLA_ERR_INVALID
+    assert call(h_kv=0) == MLA_ERR_INVALID
+    assert call(max_blocks=0) == MLA_ERR_INVALID
+    assert call(num_pages=0) == MLA_ERR_INVALID
+    assert call(new_kv=None) == MLA_ERR_INVALID
+    assert call(kc=None) == MLA_ERR_INVALID
+    assert call(lens=None) == MLA_ERR_INVALID
+    assert call(bt=None) == MLA_ERR_INVALID
+    assert call(new_lens=FAKE + 64) == MLA_ERR_INVALID  # aliases cache_seqlens
+    assert call(new_kv=FAKE + 4) == MLA_ERR_INVALID     # misaligned
+    assert call(kc=FAKE + 8) == MLA_ERR_INVALID
+    assert call(batch=1 << 20, s_new=1 << 10, h_kv=8) == MLA_ERR_UNSUPPORTED
+    assert lib.mla_last_error()
+    assert call(batch=0, new_kv=None, kc=None, lens=None, bt=None) == MLA_OK  # nothing to do, no launch

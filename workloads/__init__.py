@@ -183,6 +183,23 @@ def config_workload(index: int, seed: Optional[int] = None) -> Workload:
                          name=cfg["name"])
 
 
+def make_append_case(lens: Sequence[int], s_new: int, *, h_q: int = 16, h_kv: int = 1, seed: int = 0,
+                     extra_pages: int = 0):
+    """A cache whose block table already covers each sequence's next s_new
+    tokens, plus the rows to append: returns (w, lens_before, new_kv).
+
+    ``w`` is a causal workload with s_q = s_new and lengths lens + s_new (its
+    cache holds random rows at the new positions, which the append overwrites);
+    ``new_kv`` is bf16 bits [b, s_new, h_kv, 576], drawn after everything in w
+    from PCG64(seed + 7919)."""
+    lens_before = np.asarray(lens, dtype=np.int32)
+    w = make_workload(lens_before + s_new, s_q=max(s_new, 1), h_q=h_q, h_kv=h_kv, causal=True, seed=seed,
+                      extra_pages=extra_pages)
+    rng = np.random.Generator(np.random.PCG64(seed + 7919))
+    new_kv = bf16_bits(rng.standard_normal((len(lens_before), s_new, h_kv, D_QK), dtype=np.float32))
+    return w, lens_before, new_kv
+
+
 def permute_pages(w: Workload, seed: int) -> Workload:
     """Same logical cache with physical pages relabelled by a random permutation.
 
