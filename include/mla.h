@@ -124,7 +124,7 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int rows_per_kv, i
  *   tile_metadata, num_splits   from mla_get_metadata with the same
  *                 cache_seqlens, rows_per_kv = s_q*h_q/h_kv and num_parts
  *   causal        0/1 (bottom-right aligned when s_q > 1)
- *   softmax_scale scale applied to q.k (e.g. 1/sqrt(192))
+ *   softmax_scale scale applied to q.k (e.g. 1/sqrt(192)); finite and > 0
  *   out           bf16 bits [batch, s_q, h_q, dv]
  *   lse           fp32 [batch, s_q, h_q], natural log
  *   workspace     device scratch of at least mla_plan's workspace_bytes, holding

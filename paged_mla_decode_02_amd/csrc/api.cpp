@@ -130,7 +130,8 @@ int decode_common(int stages, const void* q, const void* kcache, int64_t num_pag
   const int rows = (int)rows_ll;
   if (int rc = check_rows(batch, rows, h_kv)) return rc;
   if (num_parts <= 0) return fail(MLA_ERR_INVALID, "num_parts must be positive (got %d)", num_parts);
-  if (!std::isfinite(softmax_scale)) return fail(MLA_ERR_INVALID, "softmax_scale must be finite");
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(MLA_ERR_INVALID, "softmax_scale must be finite and positive");
   if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID, "causal must be 0 or 1");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kcache) | reinterpret_cast<uintptr_t>(out)) & 15u)
     return fail(MLA_ERR_INVALID, "q, kcache and out must be 16-byte aligned");

@@ -581,6 +581,13 @@ constexpr int kPsLds = kPsSbuf + 2 * kPsRows * 2 * 4;
 #define MLA_QK_DMA 18
 #endif
 constexpr int kQkDma = MLA_QK_DMA;
+// transfer pieces issued during the softmax (after the QK^T ones); the rest go
+// during PV
+#ifndef MLA_SM_DMA
+#define MLA_SM_DMA 0
+#endif
+constexpr int kSmDma = MLA_SM_DMA;
+constexpr int kPvDma0 = kQkDma + kSmDma;
 
 // P row r holds 64 bf16 tokens as 8 chunks of 16 bytes; chunk c is stored at
 // position c ^ ((r >> 1) & 7), which keeps 16 consecutive rows reading the same
@@ -710,16 +717,20 @@ decode_pairsplit(DecodeParams p) {
       if (has_next) S = qk(std::true_type{});
       else S = qk(std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
-      // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page
+      // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page.
+      // Scores stay unscaled (the scale is positive, so the max commutes with
+      // it) and keys past a row's last visible one are masked only on a page
+      // that some row of the wave does not see whole.
       const int tok0 = blk * kPage + 32 * tg + 4 * hb;
+      if (__builtin_amdgcn_ballot_w64((blk + 1) * kPage > nkeys)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (tok0 + 8 * (r >> 2) + (r & 3) >= nkeys) S[r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = tok0 + 8 * (r >> 2) + (r & 3);
-        S[r] = (tok < nkeys) ? S[r] * p.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, S[r]);
-      }
-      mx = half_max(mx);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
+      mx = half_max(mx) * p.scale_log2;
       if (hb == 0) xmax[tg * kPsRows + trow] = mx;
       wg_barrier();  // both token groups' maxima visible
       mx = fmaxf(mx, xmax[(tg ^ 1) * kPsRows + trow]);
@@ -733,8 +744,12 @@ decode_pairsplit(DecodeParams p) {
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        S[r] = __builtin_amdgcn_exp2f(S[r] - m_use);
+        S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -m_use));
         ps += S[r];
+        if (kSmDma > 0 && has_next && r % 4 == 3) {
+          for (int i = kQkDma + (r / 4) * kSmDma / 4; i < kQkDma + (r / 4 + 1) * kSmDma / 4; ++i)
+            dma_piece(ndst, nrsrc, dma, i);
+        }
       }
       l_run += half_sum(ps);
 #pragma unroll
@@ -795,7 +810,8 @@ decode_pairsplit(DecodeParams p) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         if (has_next) {
-          for (int i = kQkDma + ks * (kSliceDma - kQkDma) / 4; i < kQkDma + (ks + 1) * (kSliceDma - kQkDma) / 4; ++i)
+          for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
+               ++i)
             dma_piece(ndst, nrsrc, dma, i);
         }
       }

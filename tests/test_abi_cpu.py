@@ -170,3 +170,11 @@ def test_kv_append_rejects(lib):
     assert call(batch=1 << 20, s_new=1 << 10, h_kv=8) == MLA_ERR_UNSUPPORTED
     assert lib.mla_last_error()
     assert call(batch=0, new_kv=None, kc=None, lens=None, bt=None) == MLA_OK  # nothing to do, no launch
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.5, float("inf"), float("nan")])
+def test_decode_rejects_scale(lib, scale):
+    args = [FAKE, FAKE, 100, FAKE, 8, FAKE, 4, 1, 16, 1, 576, 512, 64, FAKE, 256, FAKE, 0, scale,
+            FAKE, FAKE, FAKE, 1 << 30, None]
+    assert lib.mla_decode_paged(*args) == MLA_ERR_INVALID
+    assert b"softmax_scale" in lib.mla_last_error()
