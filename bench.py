@@ -38,7 +38,7 @@ RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 MALL_BYTES = 256 << 20
 
 
-def algorithmic(w):
+def algorithmic(w, row_bytes=576 * 2):
     """Bytes and flops the method must move / compute for one step.
 
     bytes: every valid latent+rope row once (V is reused from the same bytes),
@@ -47,7 +47,7 @@ def algorithmic(w):
     import numpy as np
     L = w.cache_seqlens.astype(np.int64)
     nb = (L + 63) // 64
-    kv = int(L.sum()) * w.h_kv * 576 * 2
+    kv = int(L.sum()) * w.h_kv * row_bytes
     qio = w.batch * w.s_q * w.h_q * (576 * 2 + 512 * 2 + 4)
     meta = int(nb.sum()) * 4 + w.batch * 4
     if w.causal:
@@ -256,6 +256,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="cache format of the decode step (fp8: the 656-byte FP8 rows, <= 16 rows per KV head)")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="--op append: rows appended per sequence (default: the workload's s_q)")
     ap.add_argument("--op", choices=["decode", "absorb", "append"], default="decode",
@@ -300,13 +302,21 @@ def main():
         return
     cfg = workloads.CONFIGS[args.config]
     w = workloads.config_workload(args.config)
-    bytes_step, flops_step, kv_bytes = algorithmic(w)
+    fp8 = args.kv == "fp8"
+    if fp8 and w.rows > 16:
+        print("--kv fp8: the FP8 cache covers s_q * h_q / h_kv <= 16 (workloads 0 and 1)", file=sys.stderr)
+        sys.exit(2)
+    bytes_step, flops_step, kv_bytes = algorithmic(w, mla.FP8_ROW_BYTES if fp8 else 576 * 2)
 
     # inputs resident in HBM; enough cache copies to defeat the MALL
-    kc_bytes = w.kcache.nbytes
+    if fp8:
+        kc_host = torch.from_numpy(workloads.make_fp8_cache(w, seed=args.config))
+    else:
+        kc_host = torch.from_numpy(w.kcache.view(np.int16))
+    kc_bytes = kc_host.numel() * kc_host.element_size()
     ncopies = max(1, math.ceil(2 * MALL_BYTES / kc_bytes))
-    kc_host = torch.from_numpy(w.kcache.view(np.int16))
-    kcs = [kc_host.to(dev).view(torch.bfloat16) for _ in range(ncopies)]
+    kcs = [kc_host.to(dev) if fp8 else kc_host.to(dev).view(torch.bfloat16) for _ in range(ncopies)]
+    decode_fn = mla.mla_decode_splitkv_fp8 if fp8 else mla.mla_decode_splitkv
     q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
     bt = torch.from_numpy(w.block_table).to(dev)
     sl = torch.from_numpy(w.cache_seqlens).to(dev)
@@ -323,7 +333,7 @@ def main():
     def step(c, evs=None):
         if evs is not None:
             evs[0].record()
-        mla.mla_decode_splitkv(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
+        decode_fn(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
         if evs is not None:
             evs[1].record()
         mla.mla_combine_splits(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
@@ -411,13 +421,14 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)}
-    traffic = traffic_from_profiles(cfg["name"], "decode")
+    traffic = None if fp8 else traffic_from_profiles(cfg["name"], "decode")
     roof["traffic"] = traffic
-    roof["kernel"] = "decode (mla_decode_splitkv)"
+    roof["kernel"] = "decode (mla_decode_splitkv_fp8)" if fp8 else "decode (mla_decode_splitkv)"
     roof["launch_ms"] = round(float(dec_ms), 5)
 
     line = {
-        "metric": "paged MLA decode bf16: achieved TB/s & TFLOPS, % of MI355X roofline",
+        "metric": ("paged MLA decode, FP8 latent cache (bf16 compute): achieved TB/s & TFLOPS, % of MI355X "
+                   "roofline") if fp8 else "paged MLA decode bf16: achieved TB/s & TFLOPS, % of MI355X roofline",
         "value": round(tbps, 4),
         "unit": "TB/s",
         "n_gpus": 1,
@@ -437,6 +448,7 @@ def main():
             "seqlens": {"kind": cfg["lens"][0], "params": list(cfg["lens"][1:]), "seed": w.seed,
                         "total_tokens": int(w.cache_seqlens.sum())},
             "softmax_scale": w.scale, "num_parts": P, "cache_copies": ncopies, "launch": mode,
+            "kv_format": "fp8_e4m3 rows of 656 B (4 power-of-two scales, bf16 rope)" if fp8 else "bf16",
         },
         "tflops": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline_frac_step": round(max(bytes_step / (HBM_PEAK_GBS * 1e9), flops_step / (BF16_PEAK_TFLOPS * 1e12))

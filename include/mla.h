@@ -65,6 +65,7 @@ extern "C" {
 #define MLA_D_QK 576
 #define MLA_DV 512
 #define MLA_METADATA_INTS 8  /* ints per tile_metadata row */
+#define MLA_FP8_ROW_BYTES 656 /* FP8 cache row: 512 e4m3 + 4 fp32 scales + 64 bf16 */
 #define MLA_MAX_BATCH 8192   /* sequences per call (metadata kernel keeps prefix sums on chip) */
 
 /*
@@ -217,6 +218,47 @@ int mla_unabsorb_out(const void* o_lat, const void* w_uv, int tokens, int h_q, v
 int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
                   const int32_t* block_table, int max_blocks, void* kcache, int64_t num_pages,
                   int32_t* new_seqlens, void* stream);
+
+/*
+ * FP8 latent cache.  The pages name FP8 as the kernel's low-precision mode
+ * (FP8/FP16 mixed precision on the FP8 instruction set, "Flash MLA: efficient
+ * MLA decoding kernel library for variable-length sequences", developer.baidu.com,
+ * §三.2, §四 step 3) but fix no format; this library's format, per token and KV
+ * head, is a 656-byte row (MLA_FP8_ROW_BYTES):
+ *   bytes   0..511  latent dims 0..511 as e4m3 (OCP E4M3FN: bias 7, 3 mantissa
+ *                   bits, largest finite 448, S.1111.111 = NaN)
+ *   bytes 512..527  4 fp32 scales, scale g for latent dims 128g .. 128g+127;
+ *                   each a power of two (the kernels use only its exponent)
+ *   bytes 528..655  rope dims 512..575 as bf16, unchanged
+ * The row stands for latent[d] = e4m3(byte d) * scale[d / 128]; with
+ * power-of-two scales every such value is a bf16 number, so dequantising is
+ * exact and the decode equals the bf16 decode of that cache.
+ *
+ * mla_kv_append_fp8: as mla_kv_append, but kcache_fp8 is uint8
+ *   [num_pages, 64, h_kv, 656] (16-byte aligned) and each bf16 row of new_kv is
+ *   quantised on the way in: scale[g] = the smallest 2^e with
+ *   max|latent[128g..128g+127]| <= 448 * 2^e (1 for an all-zero group), then
+ *   e4m3 = round-to-nearest-even(latent / 2^e).  Non-finite inputs give
+ *   unspecified bytes.  Same errors as mla_kv_append.
+ * mla_decode_paged_fp8, mla_decode_splitkv_fp8: as mla_decode_paged and
+ *   mla_decode_splitkv with kcache_fp8 in that format (the metadata, workspace
+ *   and the combine stage, mla_combine_splits, are the same); for
+ *   s_q * h_q / h_kv <= 16 (one 16-row tile per KV head), else
+ *   MLA_ERR_UNSUPPORTED.
+ */
+int mla_kv_append_fp8(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
+                      const int32_t* block_table, int max_blocks, void* kcache_fp8, int64_t num_pages,
+                      int32_t* new_seqlens, void* stream);
+int mla_decode_paged_fp8(const void* q, const void* kcache_fp8, int64_t num_pages, const int32_t* block_table,
+                         int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                         int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                         const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int mla_decode_splitkv_fp8(const void* q, const void* kcache_fp8, int64_t num_pages, const int32_t* block_table,
+                           int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                           int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                           const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Host page allocator (no GPU call).  Its whole state -- the free-page stack,

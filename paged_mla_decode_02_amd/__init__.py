@@ -33,11 +33,13 @@ import torch
 __all__ = [
     "LIB_PATH", "MlaError", "mla_plan", "mla_tile_rows", "mla_get_metadata", "mla_decode_paged",
     "mla_decode_splitkv", "mla_combine_splits", "get_mla_metadata", "flash_mla_with_kvcache",
-    "mla_absorb_q", "mla_unabsorb_out", "mla_kv_append", "Pager",
+    "mla_absorb_q", "mla_unabsorb_out", "mla_kv_append", "Pager", "mla_decode_paged_fp8",
+    "mla_decode_splitkv_fp8", "FP8_ROW_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
 PAGE_BLOCK_SIZE = 64
+FP8_ROW_BYTES = 656
 D_QK = 576
 DV = 512
 
@@ -61,7 +63,8 @@ def _load() -> ctypes.CDLL:
     lib.mla_tile_rows.restype = I
     lib.mla_get_metadata.argtypes = [P, I, I, I, I, P, P, P]
     lib.mla_get_metadata.restype = I
-    for name in ("mla_decode_paged", "mla_decode_splitkv", "mla_combine_splits"):
+    for name in ("mla_decode_paged", "mla_decode_splitkv", "mla_combine_splits", "mla_decode_paged_fp8",
+                 "mla_decode_splitkv_fp8"):
         fn = getattr(lib, name)
         fn.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
                        ctypes.c_float, P, P, P, SZ, P]
@@ -70,8 +73,9 @@ def _load() -> ctypes.CDLL:
     lib.mla_absorb_q.restype = I
     lib.mla_unabsorb_out.argtypes = [P, P, I, I, P, P]
     lib.mla_unabsorb_out.restype = I
-    lib.mla_kv_append.argtypes = [P, I, I, I, P, P, I, P, ctypes.c_int64, P, P]
-    lib.mla_kv_append.restype = I
+    for name in ("mla_kv_append", "mla_kv_append_fp8"):
+        getattr(lib, name).argtypes = [P, I, I, I, P, P, I, P, ctypes.c_int64, P, P]
+        getattr(lib, name).restype = I
     lib.mla_pager_bytes.argtypes = [I, I, I]
     lib.mla_pager_bytes.restype = SZ
     lib.mla_pager_init.argtypes = [P, SZ, I, I, I]
@@ -157,9 +161,9 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, rows_per_kv: int, h_kv: int,
 
 
 def _decode_call(fn, q, kcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,
-                 softmax_scale, out, lse, workspace):
+                 softmax_scale, out, lse, workspace, fp8=False):
     _require(q, "q", torch.bfloat16)
-    _require(kcache, "kcache", torch.bfloat16)
+    _require(kcache, "kcache", torch.uint8 if fp8 else torch.bfloat16)
     _require(block_table, "block_table", torch.int32)
     _require(cache_seqlens, "cache_seqlens", torch.int32)
     _require(tile_metadata, "tile_metadata", torch.int32)
@@ -168,8 +172,8 @@ def _decode_call(fn, q, kcache, block_table, cache_seqlens, dv, tile_metadata, n
         raise ValueError("q must be [b, s_q, h_q, d], kcache [pages, 64, h_kv, d], block_table [b, n]")
     b, s_q, h_q, d_qk = q.shape
     num_pages, page, h_kv, d_k = kcache.shape
-    if d_k != d_qk:
-        raise ValueError("q and kcache must have the same head dim")
+    if d_k != (FP8_ROW_BYTES if fp8 else d_qk):
+        raise ValueError("kcache rows must be the head dim of q (bf16) or FP8_ROW_BYTES bytes (fp8)")
     if h_kv <= 0 or h_q % h_kv:
         raise ValueError("h_q must be a multiple of h_kv")
     num_parts = tile_metadata.shape[0]
@@ -212,7 +216,24 @@ def mla_combine_splits(q, kcache, block_table, cache_seqlens, dv, tile_metadata,
                        softmax_scale, out, lse, workspace):
     """LSE combine of the partials mla_decode_splitkv left in ``workspace``."""
     return _decode_call(_lib.mla_combine_splits, q, kcache, block_table, cache_seqlens, dv, tile_metadata,
-                        num_splits, causal, softmax_scale, out, lse, workspace)
+                        num_splits, causal, softmax_scale, out, lse, workspace, fp8=kcache.dtype == torch.uint8)
+
+
+def mla_decode_paged_fp8(q: torch.Tensor, kcache_fp8: torch.Tensor, block_table: torch.Tensor,
+                         cache_seqlens: torch.Tensor, dv: int, tile_metadata: torch.Tensor,
+                         num_splits: torch.Tensor, causal: bool, softmax_scale: float,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """Paged decode over the FP8 cache (uint8 [pages, 64, h_kv, 656]); rows <= 16."""
+    return _decode_call(_lib.mla_decode_paged_fp8, q, kcache_fp8, block_table, cache_seqlens, dv, tile_metadata,
+                        num_splits, causal, softmax_scale, out, lse, workspace, fp8=True)
+
+
+def mla_decode_splitkv_fp8(q, kcache_fp8, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,
+                           softmax_scale, out, lse, workspace):
+    """Decode kernel only, FP8 cache (finish with mla_combine_splits)."""
+    return _decode_call(_lib.mla_decode_splitkv_fp8, q, kcache_fp8, block_table, cache_seqlens, dv,
+                        tile_metadata, num_splits, causal, softmax_scale, out, lse, workspace, fp8=True)
 
 
 def get_mla_metadata(cache_seqlens: torch.Tensor, num_heads_per_head_k: int, num_heads_k: int):
@@ -224,9 +245,13 @@ def flash_mla_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, block_table: 
                            cache_seqlens: torch.Tensor, head_dim_v: int, tile_metadata: torch.Tensor,
                            num_splits: torch.Tensor, softmax_scale: Optional[float] = None,
                            causal: bool = False):
-    """FlashMLA-style decode: (out, lse).  softmax_scale defaults to d_qk ** -0.5."""
+    """FlashMLA-style decode: (out, lse).  softmax_scale defaults to d_qk ** -0.5.
+    A uint8 k_cache is the FP8 format (mla_decode_paged_fp8)."""
     if softmax_scale is None:
         softmax_scale = q.shape[-1] ** -0.5
+    if k_cache.dtype == torch.uint8:
+        return mla_decode_paged_fp8(q, k_cache, block_table, cache_seqlens, head_dim_v, tile_metadata,
+                                    num_splits, causal, softmax_scale)
     return mla_decode_paged(q, k_cache, block_table, cache_seqlens, head_dim_v, tile_metadata,
                             num_splits, causal, softmax_scale)
 
@@ -287,24 +312,28 @@ def mla_unabsorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torc
 def mla_kv_append(new_kv: torch.Tensor, cache_seqlens: torch.Tensor, block_table: torch.Tensor,
                   kcache: torch.Tensor, new_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Write new_kv [b, s_new, h_kv, 576] at positions cache_seqlens[b] + j of
-    each sequence's pages (in place in kcache); returns cache_seqlens + s_new."""
+    each sequence's pages (in place in kcache); returns cache_seqlens + s_new.
+    A uint8 kcache [pages, 64, h_kv, 656] is the FP8 format: rows are quantised."""
     _require(new_kv, "new_kv", torch.bfloat16)
-    _require(kcache, "kcache", torch.bfloat16)
+    fp8 = kcache.dtype == torch.uint8
+    _require(kcache, "kcache", torch.uint8 if fp8 else torch.bfloat16)
     _require(cache_seqlens, "cache_seqlens", torch.int32)
     _require(block_table, "block_table", torch.int32)
     if new_kv.dim() != 4 or new_kv.shape[-1] != D_QK:
         raise ValueError("new_kv must be [batch, s_new, h_kv, 576]")
     b, s_new, h_kv, _ = new_kv.shape
-    if kcache.dim() != 4 or kcache.shape[1] != PAGE_BLOCK_SIZE or kcache.shape[2] != h_kv or kcache.shape[3] != D_QK:
-        raise ValueError(f"kcache must be [num_pages, 64, {h_kv}, 576]")
+    row = FP8_ROW_BYTES if fp8 else D_QK
+    if kcache.dim() != 4 or kcache.shape[1] != PAGE_BLOCK_SIZE or kcache.shape[2] != h_kv or kcache.shape[3] != row:
+        raise ValueError(f"kcache must be [num_pages, 64, {h_kv}, {row}]")
     if cache_seqlens.shape != (b,) or block_table.dim() != 2 or block_table.shape[0] != b:
         raise ValueError("cache_seqlens must be [batch] and block_table [batch, max_blocks]")
     if new_seqlens is None:
         new_seqlens = torch.empty_like(cache_seqlens)
     _require(new_seqlens, "new_seqlens", torch.int32)
-    _check(_lib.mla_kv_append(new_kv.data_ptr(), b, s_new, h_kv, cache_seqlens.data_ptr(), block_table.data_ptr(),
-                              block_table.shape[1], kcache.data_ptr(), kcache.shape[0], new_seqlens.data_ptr(),
-                              _stream(kcache.device)))
+    fn = _lib.mla_kv_append_fp8 if fp8 else _lib.mla_kv_append
+    _check(fn(new_kv.data_ptr(), b, s_new, h_kv, cache_seqlens.data_ptr(), block_table.data_ptr(),
+              block_table.shape[1], kcache.data_ptr(), kcache.shape[0], new_seqlens.data_ptr(),
+              _stream(kcache.device)))
     return new_seqlens
 
 

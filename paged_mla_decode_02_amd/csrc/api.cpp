@@ -108,7 +108,7 @@ namespace {
 
 enum Stage { kDecode = 1, kCombine = 2 };
 
-int decode_common(int stages, const void* q, const void* kcache, int64_t num_pages,
+int decode_common(int stages, int kv_fp8, const void* q, const void* kcache, int64_t num_pages,
                   const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch,
                   int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
                   const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
@@ -135,8 +135,10 @@ int decode_common(int stages, const void* q, const void* kcache, int64_t num_pag
   if (causal != 0 && causal != 1) return fail(MLA_ERR_INVALID, "causal must be 0 or 1");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kcache) | reinterpret_cast<uintptr_t>(out)) & 15u)
     return fail(MLA_ERR_INVALID, "q, kcache and out must be 16-byte aligned");
-  if ((long long)page_block_size * h_kv * MLA_D_QK * 2 > 0xffffffffLL)
+  if ((long long)page_block_size * h_kv * (kv_fp8 ? MLA_FP8_ROW_BYTES : MLA_D_QK * 2) > 0xffffffffLL)
     return fail(MLA_ERR_UNSUPPORTED, "page too large for 32-bit offsets");
+  if (kv_fp8 && mla::tile_rows_for(rows) != 16)
+    return fail(MLA_ERR_UNSUPPORTED, "the FP8 cache supports s_q * h_q / h_kv <= 16 (got %d)", rows);
   const size_t need = (size_t)(batch + num_parts) * (size_t)h_kv * (size_t)rows * (size_t)(dv + 1) * 4u;
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
@@ -168,6 +170,7 @@ int decode_common(int stages, const void* q, const void* kcache, int64_t num_pag
   p.causal = causal;
   p.scale_log2 = softmax_scale * 1.44269504088896340736f;
   p.xcd_map = (p.m_tiles * h_kv > 1 && num_parts % 8 == 0) ? 1 : 0;
+  p.kv_fp8 = kv_fp8;
 
   hipStream_t st = (hipStream_t)stream;
   if (stages & kDecode) {
@@ -190,7 +193,7 @@ int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages, const
                      int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                      const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kDecode | kCombine, q, kcache, num_pages, block_table, max_blocks, cache_seqlens,
+  return decode_common(kDecode | kCombine, 0, q, kcache, num_pages, block_table, max_blocks, cache_seqlens,
                        batch, s_q, h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts,
                        num_splits, causal, softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -200,7 +203,7 @@ int mla_decode_splitkv(const void* q, const void* kcache, int64_t num_pages, con
                        int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                        const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kDecode, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+  return decode_common(kDecode, 0, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
                        h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -210,7 +213,27 @@ int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages, con
                        int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                        const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kCombine, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+  return decode_common(kCombine, 0, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+                       h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
+                       softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_paged_fp8(const void* q, const void* kcache_fp8, int64_t num_pages, const int32_t* block_table,
+                         int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                         int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                         const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kDecode | kCombine, 1, q, kcache_fp8, num_pages, block_table, max_blocks, cache_seqlens,
+                       batch, s_q, h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits,
+                       causal, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_splitkv_fp8(const void* q, const void* kcache_fp8, int64_t num_pages, const int32_t* block_table,
+                           int max_blocks, const int32_t* cache_seqlens, int batch, int s_q, int h_q, int h_kv,
+                           int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                           const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(kDecode, 1, q, kcache_fp8, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
                        h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -253,9 +276,8 @@ int mla_unabsorb_out(const void* o_lat, const void* w_uv, int tokens, int h_q, v
 
 }  // extern "C"
 
-extern "C" {
-
-int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
+namespace {
+int append_common(int fp8, const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
                   const int32_t* block_table, int max_blocks, void* kcache, int64_t num_pages,
                   int32_t* new_seqlens, void* stream) {
   if (batch < 0 || s_new < 0) return fail(MLA_ERR_INVALID, "batch and s_new must be >= 0 (got %d, %d)", batch, s_new);
@@ -270,11 +292,32 @@ int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int3
     return fail(MLA_ERR_INVALID, "new_kv and kcache must be 16-byte aligned");
   if ((long long)batch * s_new * h_kv * (MLA_D_QK * 2 / 16) >= (1LL << 31))
     return fail(MLA_ERR_UNSUPPORTED, "batch * s_new * h_kv too large for one call");
-  hipError_t e = mla::launch_kv_append(static_cast<const uint16_t*>(new_kv), batch, s_new, h_kv, cache_seqlens,
-                                       block_table, max_blocks, static_cast<uint16_t*>(kcache), num_pages,
-                                       new_seqlens, (hipStream_t)stream);
+  hipError_t e =
+      fp8 ? mla::launch_kv_append_fp8(static_cast<const uint16_t*>(new_kv), batch, s_new, h_kv, cache_seqlens,
+                                      block_table, max_blocks, static_cast<uint8_t*>(kcache), num_pages,
+                                      new_seqlens, (hipStream_t)stream)
+          : mla::launch_kv_append(static_cast<const uint16_t*>(new_kv), batch, s_new, h_kv, cache_seqlens,
+                                  block_table, max_blocks, static_cast<uint16_t*>(kcache), num_pages, new_seqlens,
+                                  (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "kv append launch");
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
+                  const int32_t* block_table, int max_blocks, void* kcache, int64_t num_pages,
+                  int32_t* new_seqlens, void* stream) {
+  return append_common(0, new_kv, batch, s_new, h_kv, cache_seqlens, block_table, max_blocks, kcache, num_pages,
+                       new_seqlens, stream);
+}
+
+int mla_kv_append_fp8(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
+                      const int32_t* block_table, int max_blocks, void* kcache_fp8, int64_t num_pages,
+                      int32_t* new_seqlens, void* stream) {
+  return append_common(1, new_kv, batch, s_new, h_kv, cache_seqlens, block_table, max_blocks, kcache_fp8,
+                       num_pages, new_seqlens, stream);
 }
 
 }  // extern "C"

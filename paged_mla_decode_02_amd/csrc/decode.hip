@@ -204,13 +204,14 @@ __device__ __forceinline__ int page_id(int ids, int k) { return __builtin_amdgcn
 // Resource descriptor for page `blk` (physical id pid) of a sequence of length
 // L: the page's bytes for this layout, clipped to the valid tokens so slots past
 // L (and unknown page ids) read as zeros.
-__device__ __forceinline__ i32x4_t page_rsrc(const DecodeParams& p, int pid, int blk, int L) {
+__device__ __forceinline__ i32x4_t page_rsrc(const DecodeParams& p, int pid, int blk, int L,
+                                             int row_bytes = kRowBytes) {
   int valid = L - blk * kPage;
   if (valid > kPage) valid = kPage;
   const bool ok = pid >= 0 && (long long)pid < p.num_pages;
-  const long long page_stride = (long long)kPage * p.h_kv * kRowBytes;
+  const long long page_stride = (long long)kPage * p.h_kv * row_bytes;
   const char* base = (const char*)p.kcache + (ok ? (long long)pid * page_stride : 0);
-  return make_rsrc(base, ok ? (uint32_t)(valid * p.h_kv * kRowBytes) : 0u);
+  return make_rsrc(base, ok ? (uint32_t)(valid * p.h_kv * row_bytes) : 0u);
 }
 
 // Per-lane source offsets of a slice DMA: instruction (half th, group g) writes
@@ -268,6 +269,68 @@ __device__ __forceinline__ void dma_slice(LDS_AS char* dst, i32x4_t rsrc, const 
   dma_groups(dst, rsrc, d, std::make_integer_sequence<int, 9>{});
 }
 
+// FP8 cache (656-byte rows, see kF8RowBytes).  A 16-token slice moves as 656
+// token-major 16-byte chunks: 10 full transfers and one of 16 lanes; lane i of
+// transfer k supplies chunk 64k + i.  Its LDS image is dequantised into the
+// bf16 slice layout above before the slice is used, so the scoring and PV code
+// is the same for both formats.
+constexpr int kF8SliceBytes = kSlice * kF8RowBytes;             // 10496
+constexpr int kF8Chunks = kF8RowBytes / 16;                     // 41 per row
+constexpr int kF8SliceDma = (kF8SliceBytes + 1023) / 1024;      // 11
+constexpr int kF8LastLanes = (kF8SliceBytes - 1024 * (kF8SliceDma - 1)) / 16;  // 16
+struct F8Dma {
+  int off[kF8SliceDma];
+};
+__device__ __forceinline__ F8Dma fp8_dma_offsets(int tok0, int kvh, int h_kv, int lane) {
+  F8Dma d;
+#pragma unroll
+  for (int k = 0; k < kF8SliceDma; ++k) {
+    const int n = 64 * k + lane;
+    const int t = n < kSlice * kF8Chunks ? n / kF8Chunks : 0;  // lanes past the slice never transfer
+    d.off[k] = ((tok0 + t) * h_kv + kvh) * kF8RowBytes + 16 * (n - t * kF8Chunks);
+  }
+  return d;
+}
+__device__ __forceinline__ void dma_slice_fp8(LDS_AS char* dst, i32x4_t rsrc, const F8Dma& d, int lane) {
+#pragma unroll
+  for (int k = 0; k < kF8SliceDma - 1; ++k) dma16(dst + 1024 * k, rsrc, d.off[k]);
+  if (lane < kF8LastLanes) dma16(dst + 1024 * (kF8SliceDma - 1), rsrc, d.off[kF8SliceDma - 1]);
+}
+__device__ __forceinline__ unsigned cvt_fp8x2(unsigned v, float scale, bool hi_word) {
+  // e4m3 -> bf16 with a power-of-two scale (the instruction uses the scale's
+  // exponent), exact
+  return hi_word ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, true))
+                 : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, false));
+}
+// FP8 slice image (token-major rows) -> bf16 slice (swizzled).  Lane l takes
+// token l%16 and latent group l/16: 128 dims with that group's scale, plus rope
+// dims 16(l/16) .. +15 copied as they are.  With the token in the low lane bits
+// the 16 lanes of a group read 16 distinct 16-byte bank groups (rows are 656 =
+// 144 mod 256 bytes apart) and write 16 distinct ones (the slice swizzle).
+__device__ __forceinline__ void dequant_slice(const LDS_AS char* src, LDS_AS char* dst, int lane) {
+  const int t = lane & 15, g = lane >> 4;
+  const LDS_AS char* row = src + t * kF8RowBytes;
+  // every read first, so that one LDS round trip covers them all
+  u32x4_t v[8], rope[2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) v[c] = *(const LDS_AS u32x4_t*)(row + g * kF8Group + 16 * c);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) rope[c] = *(const LDS_AS u32x4_t*)(row + kLatent + 16 + 32 * g + 16 * c);
+  const float sc = *(const LDS_AS float*)(row + kLatent + 4 * g);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const u32x4_t lo = {cvt_fp8x2(v[c][0], sc, false), cvt_fp8x2(v[c][0], sc, true), cvt_fp8x2(v[c][1], sc, false),
+                        cvt_fp8x2(v[c][1], sc, true)};
+    const u32x4_t hi = {cvt_fp8x2(v[c][2], sc, false), cvt_fp8x2(v[c][2], sc, true), cvt_fp8x2(v[c][3], sc, false),
+                        cvt_fp8x2(v[c][3], sc, true)};
+    *(LDS_AS u32x4_t*)(dst + slice_off(t, 16 * g + 2 * c)) = lo;
+    *(LDS_AS u32x4_t*)(dst + slice_off(t, 16 * g + 2 * c + 1)) = hi;
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) *(LDS_AS u32x4_t*)(dst + slice_off(t, 64 + 2 * g + c)) = rope[c];
+}
+
 __device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh, int row, int& s,
                                            long long& qo) {
   s = row / p.group;
@@ -282,11 +345,21 @@ __device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh
 // sequence -- is on its way into the other LDS buffer, and the next sequence's
 // length and page ids load while the current one runs, its queries during the
 // current one's epilogue.
-// LDS: per wave two 16-token slices (2 x 18432 B) + merge statistics.
-constexpr int kTsLds = 4 * 2 * kSliceBytes + 4 * 16 * 2 * 4;
+// LDS: per wave two 16-token transfer slots + merge statistics; with the FP8
+// cache the slots hold FP8 images (2 x 10496 B) and a third region holds the
+// dequantised bf16 slice the wave computes on.
+template <bool kFp8>
+struct TsLayout {
+  static constexpr int kSlot = kFp8 ? kF8SliceBytes : kSliceBytes;
+  static constexpr int kWave = kFp8 ? 2 * kF8SliceBytes + kSliceBytes : 2 * kSliceBytes;
+  static constexpr int kDma = kFp8 ? kF8SliceDma : kSliceDma;
+  static constexpr int kLds = 4 * kWave + 4 * 16 * 2 * 4;
+};
 
+template <bool kFp8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_tokensplit(DecodeParams p) {
+  using Lay = TsLayout<kFp8>;
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
   const int lane = threadIdx.x & 63;
@@ -298,8 +371,9 @@ decode_tokensplit(DecodeParams p) {
   const int j0 = min(md[2], p.batch - 1);
   if (i0 >= p.batch || i0 < 0) return;
 
-  LDS_AS char* slices = smem + w * 2 * kSliceBytes;
-  LDS_AS float* mstat = (LDS_AS float*)(smem + 4 * 2 * kSliceBytes);  // [4 waves][16 rows][2]
+  LDS_AS char* slices = smem + w * Lay::kWave;                     // transfer slot k at k * Lay::kSlot
+  LDS_AS char* bslice = smem + w * Lay::kWave + 2 * kF8SliceBytes;  // FP8 only: dequantised slice
+  LDS_AS float* mstat = (LDS_AS float*)(smem + 4 * Lay::kWave);     // [4 waves][16 rows][2]
 
   // lane roles: QK output / PV operand B -> query row (lane & 15)
   const int r16 = lane & 15;
@@ -315,7 +389,15 @@ decode_tokensplit(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) vaddr[k] = slice_off(tt, 2 * k + ((lane & 3) >> 1)) + ((lane & 1) << 3);
   }
-  const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+  SliceDma dma;
+  F8Dma f8dma;
+  if constexpr (kFp8) f8dma = fp8_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+  else dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+  // this wave's slice of page blk (physical id pid) of a sequence of length L
+  auto issue = [&](LDS_AS char* dst, int pid, int blk_, int L_) {
+    if constexpr (kFp8) dma_slice_fp8(dst, page_rsrc(p, pid, blk_, L_, kF8RowBytes), f8dma, lane);
+    else dma_slice(dst, page_rsrc(p, pid, blk_, L_), dma);
+  };
 
   // queries: B operand of the 16x16x32 QK MFMA, 8 dims per lane per k-step.
   // Rows past the last one (a ragged tile) compute on row 0's query; every row
@@ -352,7 +434,7 @@ decode_tokensplit(DecodeParams p) {
     ids = load_page_ids(p, b, sr.lo, lane);
     vm_drain();
   }
-  if (sr.lo < sr.hi) dma_slice(slices, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+  if (sr.lo < sr.hi) issue(slices, page_id(ids, 0), sr.lo, sr.L);
   for (;;) {
     const bool has_next = b < j0;
     SeqDesc nd2 = {};
@@ -376,16 +458,20 @@ decode_tokensplit(DecodeParams p) {
       if (blk + 1 < sr.hi) {
         const int k = (blk + 1 - sr.lo) & 63;
         if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
-        dma_slice(slices + (buf ^ 1) * kSliceBytes, page_rsrc(p, page_id(ids, k), blk + 1, sr.L), dma);
-        wait_vmcnt<kSliceDma>();
+        issue(slices + (buf ^ 1) * Lay::kSlot, page_id(ids, k), blk + 1, sr.L);
+        wait_vmcnt<Lay::kDma>();
       } else if (has_next && nr.lo < nr.hi) {
-        dma_slice(slices + (buf ^ 1) * kSliceBytes, page_rsrc(p, page_id(nids, 0), nr.lo, nr.L), dma);
+        issue(slices + (buf ^ 1) * Lay::kSlot, page_id(nids, 0), nr.lo, nr.L);
         next_started = true;
-        wait_vmcnt<kSliceDma>();
+        wait_vmcnt<Lay::kDma>();
       } else {
         wait_vmcnt<0>();
       }
-      const LDS_AS char* reg = slices + buf * kSliceBytes;
+      const LDS_AS char* reg = slices + buf * Lay::kSlot;
+      if constexpr (kFp8) {
+        dequant_slice(reg, bslice, lane);
+        reg = bslice;
+      }
 
       // S^T[16 tokens x 16 rows] = K_slice . Q^T ; A-operand row = token r16,
       // chunk 4*ks + grp = group ks/2, position 4*(ks&1) + grp.  Three
@@ -473,7 +559,9 @@ decode_tokensplit(DecodeParams p) {
 
     // ---- merge the four waves' partial softmax states through LDS (the
     // buffer just consumed, buf ^ 1, of every wave), then write
-    const int dbuf = (buf ^ 1) * kSliceBytes;
+    // the merge goes through a region no transfer targets: the slot just
+    // consumed (bf16) or the dequantised slice (FP8)
+    const int dbuf = kFp8 ? 2 * kF8SliceBytes : (buf ^ 1) * kSliceBytes;
     wg_barrier();  // every wave is done with its slices
     if (lane < 16) {
       mstat[(w * 16 + lane) * 2 + 0] = m_run;
@@ -508,7 +596,7 @@ decode_tokensplit(DecodeParams p) {
     constexpr int kDumpStride = 260;  // floats per row: 256 + 4 pad
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      LDS_AS float* dump = (LDS_AS float*)(slices + dbuf);
+      LDS_AS float* dump = (LDS_AS float*)(smem + w * Lay::kWave + dbuf);
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
         *(LDS_AS f32x4_t*)(dump + r16 * kDumpStride + dt * 16 + grp * 4) = O[half * 16 + dt];
@@ -516,7 +604,7 @@ decode_tokensplit(DecodeParams p) {
       f32x4_t acc[4] = {};
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const LDS_AS float* src = (const LDS_AS float*)(smem + v * 2 * kSliceBytes + dbuf);
+        const LDS_AS float* src = (const LDS_AS float*)(smem + v * Lay::kWave + dbuf);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           acc[k] += *(const LDS_AS f32x4_t*)(src + rr * kDumpStride + w * 64 + (lane & 3) * 16 + k * 4);
@@ -556,7 +644,7 @@ decode_tokensplit(DecodeParams p) {
     ids = nids;
     nr = seq_range(p, nd2, b + 1, i0, f0, j0, e0, ord0);
     nids = nids2;
-    if (!next_started && sr.lo < sr.hi) dma_slice(slices + buf * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+    if (!next_started && sr.lo < sr.hi) issue(slices + buf * Lay::kSlot, page_id(ids, 0), sr.lo, sr.L);
   }
 }
 
@@ -878,7 +966,11 @@ hipError_t launch_one(K kernel, int lds, const DecodeParams& p, hipStream_t stre
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  if (tile_rows_for(p.rows) == 16) return launch_one(decode_tokensplit, kTsLds, p, stream);
+  if (tile_rows_for(p.rows) == 16) {
+    if (p.kv_fp8) return launch_one(decode_tokensplit<true>, TsLayout<true>::kLds, p, stream);
+    return launch_one(decode_tokensplit<false>, TsLayout<false>::kLds, p, stream);
+  }
+  if (p.kv_fp8) return hipErrorInvalidValue;  // the 64-row kernel reads bf16 pages only
   return launch_one(decode_pairsplit, kPsLds, p, stream);
 }
 

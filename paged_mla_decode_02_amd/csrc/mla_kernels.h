@@ -17,6 +17,10 @@ constexpr int kRope = 64;          // rope dims (kDqk = kLatent + kRope)
 constexpr int kLatent = 512;       // compressed latent width (= kDv)
 constexpr int kDvOut = 128;        // value dims per head after W_UV
 constexpr int kMaxBatch = 8192;
+// FP8 cache row: 512 e4m3 latent dims, 4 fp32 power-of-two scales (one per 128
+// latent dims), 64 bf16 rope dims = 656 bytes.
+constexpr int kF8Group = 128;
+constexpr int kF8RowBytes = kLatent + 4 * (kLatent / kF8Group) + 2 * kRope;
 
 // Query rows one workgroup owns: <= 16 rows use the 16-row token-split kernel,
 // larger row counts the 64-row pair-split kernel (ceil(rows / 64) row tiles).
@@ -43,6 +47,7 @@ struct DecodeParams {
   int batch, s_q, h_q, h_kv, rows, group, max_blocks, num_parts, m_tiles, causal;
   float scale_log2;          // softmax_scale * log2(e)
   int xcd_map;               // workgroup -> (part, row tile, kv head) mapping keeps a part on one XCD
+  int kv_fp8;                // kcache rows are the 656-byte FP8 format (kF8RowBytes) instead of bf16
 };
 
 // Records the status of the last C-ABI call on this thread (message for
@@ -58,6 +63,9 @@ hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const
 hipError_t launch_kv_append(const uint16_t* new_kv, int batch, int s_new, int h_kv, const int32_t* seqlens,
                             const int32_t* block_table, int max_blocks, uint16_t* kcache, long long num_pages,
                             int32_t* new_seqlens, hipStream_t stream);
+hipError_t launch_kv_append_fp8(const uint16_t* new_kv, int batch, int s_new, int h_kv, const int32_t* seqlens,
+                                const int32_t* block_table, int max_blocks, uint8_t* kcache, long long num_pages,
+                                int32_t* new_seqlens, hipStream_t stream);
 hipError_t launch_unabsorb_out(const uint16_t* o_lat, const uint16_t* w_uv, int tokens, int h_q, uint16_t* out,
                                hipStream_t stream);
 

@@ -1,0 +1,153 @@
+"""GPU parity of the FP8 cache path through the C ABI.
+
+* mla_kv_append_fp8 quantises bf16 rows on the GPU: the whole cache after the
+  append must equal, byte for byte, the oracle quantiser's rows scattered by the
+  append oracle (integer work: bit-exact bar).
+* mla_decode_paged_fp8 against the fp64 decode oracle run on the exact bf16
+  values the FP8 cache stands for (oracle/fp8.py dequantises; power-of-two
+  scales make that exact): out rel-L2 <= 1e-2, lse abs <= 1e-3, as for bf16.
+The FP8 caches are drawn directly in the format (workloads.make_fp8_cache), and
+slots past a sequence's end hold NaN codes, which must never reach a result.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads
+from workloads import make_append_case, make_workload
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import oracle
+    from oracle import fp8, paging
+    import paged_mla_decode_02_amd as mla
+    oracle.build(force=False)
+    return torch, mla, oracle.default(), fp8, paging, torch.device("cuda:0")
+
+
+def poison_tails(w, kc8):
+    """NaN codes in every latent byte of every slot past a sequence's end."""
+    kc8 = kc8.copy()
+    used = np.zeros(kc8.shape[:2], dtype=bool)
+    for i, L in enumerate(w.cache_seqlens):
+        for t in range(int(L)):
+            used[w.block_table[i, t // 64], t % 64] = True
+    kc8[~used, :, :512] = 0x7F
+    return kc8
+
+
+def decode_fp8(env, w, kc8, num_parts=None):
+    torch, mla, _, _, _, dev = env
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kc = torch.from_numpy(kc8).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.cache_seqlens).to(dev)
+    md, ns = mla.mla_get_metadata(sl, w.rows, w.h_kv, num_parts=num_parts)
+    out, lse = mla.mla_decode_paged_fp8(q, kc, bt, sl, w.dv, md, ns, w.causal, w.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    return o.reshape(-1, o.shape[-1]), lse.cpu().numpy().astype(np.float64).reshape(-1)
+
+
+def check(go, gl, ro, rl, what):
+    ninf = np.isneginf(rl)
+    assert np.all(np.isfinite(go)), what
+    assert np.array_equal(np.isneginf(gl), ninf), what
+    rel = np.linalg.norm(go - ro) / np.linalg.norm(ro)
+    err = np.max(np.abs(gl[~ninf] - rl[~ninf]))
+    assert rel <= OUT_TOL and err <= LSE_TOL, f"{what}: rel {rel:.2e} lse {err:.2e}"
+
+
+@pytest.mark.parametrize("lens,s_q,h_q,h_kv,causal,parts", [
+    ([218, 164], 1, 16, 1, False, None),
+    ([1, 70, 300], 2, 8, 1, True, None),
+    ([0, 129, 64], 1, 32, 2, False, None),
+    ([1000, 3, 577], 1, 16, 1, False, 7),     # forced splits: the combine on FP8 partials
+])
+def test_decode_fp8_small(env, lens, s_q, h_q, h_kv, causal, parts):
+    _, _, orc, fp8, _, _ = env
+    w = make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal, seed=sum(lens) + h_q)
+    kc8 = poison_tails(w, workloads.make_fp8_cache(w, seed=len(lens)))
+    go, gl = decode_fp8(env, w, kc8, num_parts=parts)
+    # the oracle sees the exact bf16 values (NaN codes only where no sequence reads)
+    clean = kc8.copy()
+    lat = clean[..., :512]
+    lat[lat == 0x7F] = 0
+    deq = fp8.bf16_cache(clean)
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=deq))
+    check(go, gl, ro, rl, f"{lens}")
+
+
+def test_decode_fp8_full_size_sampled(env):
+    _, _, orc, fp8, _, _ = env
+    w = workloads.config_workload(1)
+    kc8 = workloads.make_fp8_cache(w, seed=1)
+    go, gl = decode_fp8(env, w, kc8)
+    rng = np.random.default_rng(11)
+    n = w.batch * w.s_q * w.h_q
+    sel = np.sort(rng.choice(n, size=48, replace=False))
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(kc8)), sel=sel)
+    check(go[sel], gl[sel], ro, rl, "memory_bound_varlen fp8")
+
+
+def test_fp8_rejects_64_row_tiles(env):
+    torch, mla, _, _, _, dev = env
+    w = make_workload([64], s_q=1, h_q=64, seed=2)
+    with pytest.raises(mla.MlaError) as e:
+        decode_fp8(env, w, workloads.make_fp8_cache(w, seed=2))
+    assert e.value.code == -2
+
+
+@pytest.mark.parametrize("lens,s_new,h_kv", [([0, 1, 63, 64, 130], 1, 1), ([5, 62, 200], 3, 2),
+                                             ([0, 0], 70, 1)])
+def test_append_fp8_bit_exact(env, lens, s_new, h_kv):
+    torch, mla, _, fp8, paging, dev = env
+    w, before, new_kv = make_append_case(lens, s_new, h_kv=h_kv, h_q=2 * h_kv, seed=len(lens) + 5,
+                                         extra_pages=2)
+    # rows that stress the quantiser: an all-zero group, exact ties, a wide range
+    nk = workloads.bf16_to_f32(new_kv)
+    nk[0, 0, 0, 0:128] = 0.0
+    nk[0, 0, 0, 128] = 448.0
+    nk[0, 0, 0, 129:133] = [1.0625, 1.1875, -1.0625, 232.0]
+    if nk.shape[1] > 1:
+        nk[0, 1, 0, :512] *= np.float32(2.0 ** -30)
+    new_kv = workloads.bf16_bits(nk)
+    kc8 = workloads.make_fp8_cache(w, seed=3)
+    kc = torch.from_numpy(kc8).to(dev)
+    sl = torch.from_numpy(before).to(dev)
+    out_lens = mla.mla_kv_append(torch.from_numpy(new_kv.view(np.int16)).to(dev).view(torch.bfloat16), sl,
+                                 torch.from_numpy(w.block_table).to(dev), kc)
+    torch.cuda.synchronize()
+    ref, ref_lens = paging.kv_append(kc8, w.block_table, before, fp8.quantize_rows(new_kv))
+    got = kc.cpu().numpy()
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} bytes differ"
+    assert np.array_equal(out_lens.cpu().numpy(), ref_lens)
+
+
+def test_append_fp8_then_decode(env):
+    """quantise on append -> FP8 decode == bf16 oracle on the dequantised cache."""
+    torch, mla, orc, fp8, paging, dev = env
+    w, before, new_kv = make_append_case([300, 5, 64], 1, h_q=16, seed=9)
+    kc8 = workloads.make_fp8_cache(w, seed=9)
+    kc = torch.from_numpy(kc8).to(dev)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    new_lens = mla.mla_kv_append(torch.from_numpy(new_kv.view(np.int16)).to(dev).view(torch.bfloat16),
+                                 torch.from_numpy(before).to(dev), bt, kc)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    md, ns = mla.get_mla_metadata(new_lens, w.rows, 1)
+    out, lse = mla.flash_mla_with_kvcache(q, kc, bt, new_lens, 512, md, ns, causal=True, softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    ref8, lens2 = paging.kv_append(kc8, w.block_table, before, fp8.quantize_rows(new_kv))
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(ref8), cache_seqlens=lens2))
+    o = out.float().cpu().numpy().astype(np.float64).reshape(-1, 512)
+    check(o, lse.cpu().numpy().astype(np.float64).reshape(-1), ro, rl, "append fp8 -> decode")

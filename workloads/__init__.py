@@ -200,6 +200,32 @@ def make_append_case(lens: Sequence[int], s_new: int, *, h_q: int = 16, h_kv: in
     return w, lens_before, new_kv
 
 
+FP8_ROW_BYTES = 656
+
+
+def make_fp8_cache(w: Workload, seed: int, scale_exp: int = -2) -> np.ndarray:
+    """A random cache in the 656-byte FP8 row format with w's shape: uint8
+    [pages, 64, h_kv, 656].  Latent bytes are e4m3 codes with random sign,
+    exponent field 4..10 and mantissa (values 2^-3 .. 3.75 before scaling), one
+    in 16 of them zero; the four scales of a row are 2^(scale_exp + u), u in
+    {-1, 0, 1}; the rope dims are w's rope bits.  Drawn from PCG64(seed + 104729)
+    in that order; nothing here quantises."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    shape = w.kcache.shape[:-1]
+    n = int(np.prod(shape))
+    sign = rng.integers(0, 2, size=(n, 512), dtype=np.uint8) << 7
+    ex = rng.integers(4, 11, size=(n, 512), dtype=np.uint8)
+    man = rng.integers(0, 8, size=(n, 512), dtype=np.uint8)
+    codes = sign | (ex << 3) | man
+    codes[rng.random((n, 512)) < 1.0 / 16] = 0
+    scales = np.ldexp(np.float32(1.0), scale_exp + rng.integers(-1, 2, size=(n, 4))).astype(np.float32)
+    out = np.empty((n, FP8_ROW_BYTES), dtype=np.uint8)
+    out[:, :512] = codes
+    out[:, 512:528] = scales.view(np.uint8).reshape(n, 16)
+    out[:, 528:] = np.ascontiguousarray(w.kcache.reshape(n, D_QK)[:, 512:]).view(np.uint8).reshape(n, 128)
+    return out.reshape(shape + (FP8_ROW_BYTES,))
+
+
 def permute_pages(w: Workload, seed: int) -> Workload:
     """Same logical cache with physical pages relabelled by a random permutation.
 
