@@ -247,6 +247,101 @@ def bench_append(args, torch, mla, workloads, dev):
     print(json.dumps(line))
 
 
+def bench_sparse(args, torch, mla, workloads, dev):
+    """Token-sparse decode: 64 sequences of U[4096, 16384] tokens, 128 query
+    heads, each query attending to a top-2048 selection (uniform distinct
+    positions).  A step is the decode of the kept rows (decode + combine), as
+    graph replays; the preparation (list -> row offsets) and the schedule run
+    once per step in use and are timed on their own."""
+    import numpy as np
+    rng = np.random.default_rng(20)
+    lens = rng.integers(4096, 16385, size=64)
+    w = workloads.make_workload(lens, s_q=1, h_q=128, seed=20, name="sparse_topk2048")
+    idx, ptr = workloads.make_sparse_indices(w, args.topk, seed=20)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    kc_host = torch.from_numpy(w.kcache.view(np.int16))
+    ncopies = max(1, math.ceil(2 * MALL_BYTES / w.kcache.nbytes))
+    kcs = [kc_host.to(dev).view(torch.bfloat16) for _ in range(ncopies)]
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.cache_seqlens).to(dev)
+    ti = torch.from_numpy(idx).to(dev)
+    tp = torch.from_numpy(ptr).to(dev)
+    offs, counts = mla.mla_sparse_prepare(ti, tp, 1, bt, sl, w.num_pages, 1)
+    rows = w.h_q
+    P, ws_bytes = mla.mla_plan(w.batch, rows, 1)
+    md, ns = mla.mla_get_metadata(counts, rows, 1, num_parts=P)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, 1, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.batch, 1, w.h_q), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    kept = int(counts.sum().item())
+    by = kept * 576 * 2 + w.batch * w.h_q * (576 * 2 + 512 * 2 + 4) + kept * 4
+    fl = 2 * kept * w.h_q * (576 + 512)
+
+    def step(c):
+        mla.mla_sparse_decode(q, kcs[c], offs, tp, counts, 512, md, ns, w.scale, out, lse, ws)
+
+    for c in range(min(3, ncopies)):
+        step(c)
+    torch.cuda.synchronize()
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(s_):
+        for c in range(ncopies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s_):
+                step(c)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(s_)
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        graphs[i % ncopies].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        graphs[i % ncopies].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    n_ev = min(K, 50)
+
+    def timed(fn):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+        torch.cuda._sleep(int(20e6))
+        for i in range(n_ev):
+            evs[i][0].record()
+            fn(i)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_step = timed(lambda i: step(i % ncopies))
+    t_prep = timed(lambda i: mla.mla_sparse_prepare(ti, tp, 1, bt, sl, w.num_pages, 1, offsets=offs, counts=counts))
+    t_md = timed(lambda i: mla.mla_get_metadata(counts, rows, 1, num_parts=P, out=(md, ns)))
+    tf = fl / (t_step * 1e-3) / 1e12
+    gbs = by / (t_step * 1e-3) / 1e9
+    bound = "hbm" if fl / by < RIDGE else "mfma"
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)} if bound == "hbm" else
+            {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+    roof.update({"traffic": None, "kernel": "sparse decode + combine (mla_sparse_decode)"})
+    line = {
+        "metric": "token-sparse MLA decode bf16 (top-k rows per query): achieved TB/s & TFLOPS",
+        "value": round(by / (ms * 1e-3) / 1e12, 4), "unit": "TB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "sparse_topk", "batch": w.batch, "s_q": 1, "h_q": w.h_q, "h_kv": 1,
+                   "topk": args.topk, "seqlens": "uniform [4096, 16384], seed 20", "kept_rows": kept,
+                   "num_parts": P, "cache_copies": ncopies},
+        "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+        "algorithmic": {"bytes_per_step": by, "flops_per_step": fl},
+        "kernel_ms": {"decode_step": round(t_step, 5), "prepare": round(t_prep, 5), "metadata": round(t_md, 5),
+                      "launches": n_ev},
+        "roofline": roof,
+    }
+    print(json.dumps(line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,7 +355,8 @@ def main():
                     help="cache format of the decode step (fp8: the 656-byte FP8 rows, <= 16 rows per KV head)")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="--op append: rows appended per sequence (default: the workload's s_q)")
-    ap.add_argument("--op", choices=["decode", "absorb", "append"], default="decode",
+    ap.add_argument("--topk", type=int, default=2048, help="--op sparse: entries selected per query")
+    ap.add_argument("--op", choices=["decode", "absorb", "append", "sparse"], default="decode",
                     help="decode (default): the decode step; absorb: the two absorption GEMMs of the "
                          "workload's query tokens and heads (one JSON line of their own)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -299,6 +395,9 @@ def main():
         return
     if args.op == "append":
         bench_append(args, torch, mla, workloads, dev)
+        return
+    if args.op == "sparse":
+        bench_sparse(args, torch, mla, workloads, dev)
         return
     cfg = workloads.CONFIGS[args.config]
     w = workloads.config_workload(args.config)

@@ -261,6 +261,46 @@ int mla_decode_splitkv_fp8(const void* q, const void* kcache_fp8, int64_t num_pa
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Token-sparse decode.  The "Flash MLA: efficient MLA decoding kernel library
+ * for variable-length sequences" page (developer.baidu.com, §三.3) adds a
+ * token-level sparse mode: each query keeps only its top-k key tokens, the
+ * selection stored in CSR form.  How the tokens are scored and picked is the
+ * caller's (the page's description of it is garbled); these calls take the
+ * selection.  Query row v = b * s_q + s (batch b, query token s) attends, with
+ * every head, to the cached tokens of sequence b listed in
+ * indices[indptr[v] .. indptr[v+1]) (logical positions); entries outside
+ * [0, cache_seqlens[b]) or on a page id outside [0, num_pages) are ignored,
+ * listed duplicates count once per listing, and there is no causal mask (the
+ * list decides).  A row with no kept entry gives out = 0, lse = -inf.
+ *
+ * mla_sparse_prepare: keeps the valid entries of every row, in order, as the
+ *   byte offsets of their cache rows (KV head 0): offsets[indptr[v] + i] for
+ *   i < counts[v].
+ *   indices  int32 [indptr[batch*s_q]] device
+ *   indptr   int32 [batch*s_q + 1] device, non-decreasing, indptr[0] = 0
+ *   block_table, cache_seqlens, num_pages, max_blocks, h_kv: as for the decode
+ *   offsets  uint32 [indptr[batch*s_q] + 64] device, out (the 64 spare entries
+ *            keep the decode's page-wide reads inside the array)
+ *   counts   int32 [batch*s_q] device, out
+ * mla_sparse_decode: the decode over those rows.  The schedule comes from
+ *   mla_plan(batch*s_q, h_q/h_kv, h_kv, ...) and
+ *   mla_get_metadata(counts, batch*s_q, h_q/h_kv, h_kv, ...): every query row is
+ *   a sequence of counts[v] keys.  q, out, lse as for mla_decode_paged.  Uses
+ *   the 64-row kernel for any h_q/h_kv.
+ * The cache must hold at most 0xE0000000 bytes (32-bit row offsets), else
+ * MLA_ERR_UNSUPPORTED; batch*s_q <= MLA_MAX_BATCH for the decode.  Other
+ * errors as for mla_decode_paged.
+ */
+int mla_sparse_prepare(const int32_t* indices, const int32_t* indptr, int batch, int s_q,
+                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int64_t num_pages,
+                       int h_kv, uint32_t* offsets, int32_t* counts, void* stream);
+int mla_sparse_decode(const void* q, const void* kcache, int64_t num_pages, const uint32_t* offsets,
+                      const int32_t* indptr, const int32_t* counts, int batch, int s_q, int h_q, int h_kv,
+                      int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                      const int32_t* num_splits, float softmax_scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
  * Host page allocator (no GPU call).  Its whole state -- the free-page stack,
  * the owner of every physical page and the per-sequence page tables, which are
  * the rows of a host block table [max_seqs, max_blocks] int32 (-1 = no page) --

@@ -9,6 +9,12 @@ The paged cache (same names as the C ABI):
     mla_kv_append(new_kv, cache_seqlens, block_table, kcache) -> new_seqlens
     Pager(num_pages, max_seqs, max_blocks): host page allocator (reserve,
         release, block_table)
+Token-sparse decode (same names as the C ABI):
+    mla_sparse_prepare(indices, indptr, s_q, block_table, cache_seqlens, num_pages, h_kv)
+        -> (row offsets, counts)
+    mla_sparse_decode(q, kcache, offsets, indptr, counts, dv, tile_metadata, num_splits, scale)
+    flash_mla_sparse_with_kvcache(q, k_cache, block_table, cache_seqlens, indices, indptr)
+        -> (out, lse): prepare + schedule + decode
 The absorption GEMMs around the decode (same names as the C ABI):
     mla_absorb_q(q_nope, q_rope, w_uk) -> q_abs      (the decode's query)
     mla_unabsorb_out(o_lat, w_uv) -> out             (per-head values)
@@ -34,7 +40,8 @@ __all__ = [
     "LIB_PATH", "MlaError", "mla_plan", "mla_tile_rows", "mla_get_metadata", "mla_decode_paged",
     "mla_decode_splitkv", "mla_combine_splits", "get_mla_metadata", "flash_mla_with_kvcache",
     "mla_absorb_q", "mla_unabsorb_out", "mla_kv_append", "Pager", "mla_decode_paged_fp8",
-    "mla_decode_splitkv_fp8", "FP8_ROW_BYTES",
+    "mla_decode_splitkv_fp8", "FP8_ROW_BYTES", "mla_sparse_prepare", "mla_sparse_decode",
+    "flash_mla_sparse_with_kvcache",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -76,6 +83,11 @@ def _load() -> ctypes.CDLL:
     for name in ("mla_kv_append", "mla_kv_append_fp8"):
         getattr(lib, name).argtypes = [P, I, I, I, P, P, I, P, ctypes.c_int64, P, P]
         getattr(lib, name).restype = I
+    lib.mla_sparse_prepare.argtypes = [P, P, I, I, P, I, P, ctypes.c_int64, I, P, P, P]
+    lib.mla_sparse_prepare.restype = I
+    lib.mla_sparse_decode.argtypes = [P, P, ctypes.c_int64, P, P, P, I, I, I, I, I, I, I, P, I, P, ctypes.c_float,
+                                      P, P, P, SZ, P]
+    lib.mla_sparse_decode.restype = I
     lib.mla_pager_bytes.argtypes = [I, I, I]
     lib.mla_pager_bytes.restype = SZ
     lib.mla_pager_init.argtypes = [P, SZ, I, I, I]
@@ -381,3 +393,78 @@ class Pager:
         n = self.max_seqs * self.max_blocks
         arr = (ctypes.c_int32 * n).from_address(ctypes.addressof(p.contents))
         return torch.frombuffer(bytearray(arr), dtype=torch.int32).reshape(self.max_seqs, self.max_blocks)
+
+
+def mla_sparse_prepare(indices: torch.Tensor, indptr: torch.Tensor, s_q: int, block_table: torch.Tensor,
+                       cache_seqlens: torch.Tensor, num_pages: int, h_kv: int,
+                       offsets: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None):
+    """Keep each query row's valid index entries as cache-row byte offsets.
+
+    indices int32 [nnz] (logical positions), indptr int32 [batch*s_q + 1] (CSR);
+    returns (offsets uint32-as-int32 [nnz + 64], counts int32 [batch*s_q])."""
+    for t, n in ((indices, "indices"), (indptr, "indptr"), (block_table, "block_table"),
+                 (cache_seqlens, "cache_seqlens")):
+        _require(t, n, torch.int32)
+    b = cache_seqlens.shape[0]
+    rows = indptr.shape[0] - 1
+    if rows != b * s_q:
+        raise ValueError("indptr must have batch * s_q + 1 entries")
+    dev = indices.device
+    if offsets is None:
+        offsets = torch.empty(indices.shape[0] + 64, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(rows, dtype=torch.int32, device=dev)
+    _require(offsets, "offsets", torch.int32)
+    _require(counts, "counts", torch.int32)
+    if offsets.shape[0] < indices.shape[0] + 64:
+        raise ValueError("offsets needs nnz + 64 entries")
+    _check(_lib.mla_sparse_prepare(indices.data_ptr(), indptr.data_ptr(), b, s_q, block_table.data_ptr(),
+                                   block_table.shape[1], cache_seqlens.data_ptr(), num_pages, h_kv,
+                                   offsets.data_ptr(), counts.data_ptr(), _stream(dev)))
+    return offsets, counts
+
+
+def mla_sparse_decode(q: torch.Tensor, kcache: torch.Tensor, offsets: torch.Tensor, indptr: torch.Tensor,
+                      counts: torch.Tensor, dv: int, tile_metadata: torch.Tensor, num_splits: torch.Tensor,
+                      softmax_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None):
+    """Decode of every query row over its kept cache rows (after mla_sparse_prepare)."""
+    _require(q, "q", torch.bfloat16)
+    _require(kcache, "kcache", torch.bfloat16)
+    for t, n in ((offsets, "offsets"), (indptr, "indptr"), (counts, "counts"), (tile_metadata, "tile_metadata"),
+                 (num_splits, "num_splits")):
+        _require(t, n, torch.int32)
+    b, s_q, h_q, d_qk = q.shape
+    num_pages, page, h_kv, d_k = kcache.shape
+    if d_k != d_qk or h_q % h_kv:
+        raise ValueError("q / kcache shapes do not match")
+    rows = h_q // h_kv
+    num_parts = tile_metadata.shape[0]
+    dev = q.device
+    if out is None:
+        out = torch.empty((b, s_q, h_q, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty((b * s_q + num_parts) * h_kv * rows * (dv + 1) * 4, dtype=torch.uint8, device=dev)
+    _check(_lib.mla_sparse_decode(q.data_ptr(), kcache.data_ptr(), num_pages, offsets.data_ptr(), indptr.data_ptr(),
+                                  counts.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
+                                  num_parts, num_splits.data_ptr(), float(softmax_scale), out.data_ptr(),
+                                  lse.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(dev)))
+    return out, lse
+
+
+def flash_mla_sparse_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, block_table: torch.Tensor,
+                                  cache_seqlens: torch.Tensor, indices: torch.Tensor, indptr: torch.Tensor,
+                                  head_dim_v: int = DV, softmax_scale: Optional[float] = None,
+                                  num_parts: Optional[int] = None):
+    """Token-sparse decode: query row b*s_q+s attends to the cached tokens listed
+    in indices[indptr[v]:indptr[v+1]].  Returns (out, lse)."""
+    if softmax_scale is None:
+        softmax_scale = q.shape[-1] ** -0.5
+    b, s_q, h_q, _ = q.shape
+    h_kv = k_cache.shape[2]
+    offsets, counts = mla_sparse_prepare(indices, indptr, s_q, block_table, cache_seqlens, k_cache.shape[0], h_kv)
+    md, ns = mla_get_metadata(counts, h_q // h_kv, h_kv, num_parts=num_parts)
+    return mla_sparse_decode(q, k_cache, offsets, indptr, counts, head_dim_v, md, ns, softmax_scale)

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmla.so")
-SOURCES = ["api.cpp", "pager.cpp", "sched.hip", "decode.hip", "combine.hip", "absorb.hip", "kv_append.hip"]
+SOURCES = ["api.cpp", "pager.cpp", "sched.hip", "decode.hip", "combine.hip", "absorb.hip", "kv_append.hip", "sparse.hip"]
 ARCH = "gfx950"
 
 

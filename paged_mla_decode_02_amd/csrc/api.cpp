@@ -108,20 +108,26 @@ namespace {
 
 enum Stage { kDecode = 1, kCombine = 2 };
 
-int decode_common(int stages, int kv_fp8, const void* q, const void* kcache, int64_t num_pages,
+struct SparseArgs {
+  const uint32_t* offsets;
+  const int32_t* indptr;
+};
+
+int decode_common(int stages, int kv_fp8, const SparseArgs* sp, const void* q, const void* kcache, int64_t num_pages,
                   const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch,
                   int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
                   const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
                   float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                   void* stream) {
-  if (!q || !kcache || !block_table || !cache_seqlens || !tile_metadata || !num_splits || !out || !lse)
+  if (!q || !kcache || (!block_table && !sp) || !cache_seqlens || !tile_metadata || !num_splits || !out || !lse)
     return fail(MLA_ERR_INVALID, "null pointer argument");
+  if (sp && (!sp->offsets || !sp->indptr)) return fail(MLA_ERR_INVALID, "null pointer argument");
   if (d_qk != MLA_D_QK) return fail(MLA_ERR_UNSUPPORTED, "d_qk must be %d (got %d)", MLA_D_QK, d_qk);
   if (dv != MLA_DV) return fail(MLA_ERR_UNSUPPORTED, "dv must be %d (got %d)", MLA_DV, dv);
   if (page_block_size != MLA_PAGE_BLOCK_SIZE)
     return fail(MLA_ERR_UNSUPPORTED, "page_block_size must be %d (got %d)", MLA_PAGE_BLOCK_SIZE,
                 page_block_size);
-  if (s_q <= 0 || h_q <= 0 || h_kv <= 0 || max_blocks <= 0 || num_pages <= 0)
+  if (s_q <= 0 || h_q <= 0 || h_kv <= 0 || (max_blocks <= 0 && !sp) || num_pages <= 0)
     return fail(MLA_ERR_INVALID, "sizes must be positive (s_q=%d h_q=%d h_kv=%d max_blocks=%d num_pages=%lld)",
                 s_q, h_q, h_kv, max_blocks, (long long)num_pages);
   if (h_q % h_kv != 0) return fail(MLA_ERR_INVALID, "h_q (%d) must be a multiple of h_kv (%d)", h_q, h_kv);
@@ -171,6 +177,15 @@ int decode_common(int stages, int kv_fp8, const void* q, const void* kcache, int
   p.scale_log2 = softmax_scale * 1.44269504088896340736f;
   p.xcd_map = (p.m_tiles * h_kv > 1 && num_parts % 8 == 0) ? 1 : 0;
   p.kv_fp8 = kv_fp8;
+  if (sp) {
+    const long long cache_bytes = num_pages * (long long)MLA_PAGE_BLOCK_SIZE * h_kv * MLA_D_QK * 2;
+    if (cache_bytes > (long long)mla::kSparseMaxCacheBytes)
+      return fail(MLA_ERR_UNSUPPORTED, "the sparse decode addresses caches up to %u bytes", mla::kSparseMaxCacheBytes);
+    p.sparse = 1;
+    p.sp_offs = sp->offsets;
+    p.sp_rowptr = sp->indptr;
+    p.sp_cache_bytes = (uint32_t)cache_bytes;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   if (stages & kDecode) {
@@ -193,7 +208,7 @@ int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages, const
                      int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                      const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kDecode | kCombine, 0, q, kcache, num_pages, block_table, max_blocks, cache_seqlens,
+  return decode_common(kDecode | kCombine, 0, nullptr, q, kcache, num_pages, block_table, max_blocks, cache_seqlens,
                        batch, s_q, h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts,
                        num_splits, causal, softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -203,7 +218,7 @@ int mla_decode_splitkv(const void* q, const void* kcache, int64_t num_pages, con
                        int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                        const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kDecode, 0, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+  return decode_common(kDecode, 0, nullptr, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
                        h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -213,7 +228,7 @@ int mla_combine_splits(const void* q, const void* kcache, int64_t num_pages, con
                        int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                        const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kCombine, 0, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+  return decode_common(kCombine, 0, nullptr, q, kcache, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
                        h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -223,7 +238,7 @@ int mla_decode_paged_fp8(const void* q, const void* kcache_fp8, int64_t num_page
                          int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                          const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                          void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kDecode | kCombine, 1, q, kcache_fp8, num_pages, block_table, max_blocks, cache_seqlens,
+  return decode_common(kDecode | kCombine, 1, nullptr, q, kcache_fp8, num_pages, block_table, max_blocks, cache_seqlens,
                        batch, s_q, h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits,
                        causal, softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -233,7 +248,7 @@ int mla_decode_splitkv_fp8(const void* q, const void* kcache_fp8, int64_t num_pa
                            int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
                            const int32_t* num_splits, int causal, float softmax_scale, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_common(kDecode, 1, q, kcache_fp8, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
+  return decode_common(kDecode, 1, nullptr, q, kcache_fp8, num_pages, block_table, max_blocks, cache_seqlens, batch, s_q,
                        h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, causal,
                        softmax_scale, out, lse, workspace, workspace_bytes, stream);
 }
@@ -318,6 +333,42 @@ int mla_kv_append_fp8(const void* new_kv, int batch, int s_new, int h_kv, const 
                       int32_t* new_seqlens, void* stream) {
   return append_common(1, new_kv, batch, s_new, h_kv, cache_seqlens, block_table, max_blocks, kcache_fp8,
                        num_pages, new_seqlens, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int mla_sparse_prepare(const int32_t* indices, const int32_t* indptr, int batch, int s_q,
+                       const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int64_t num_pages,
+                       int h_kv, uint32_t* offsets, int32_t* counts, void* stream) {
+  if (batch < 0 || s_q <= 0 || h_kv <= 0 || max_blocks <= 0 || num_pages <= 0)
+    return fail(MLA_ERR_INVALID, "batch >= 0 and s_q, h_kv, max_blocks, num_pages > 0 required");
+  if (batch == 0) return ok();
+  if (!indices || !indptr || !block_table || !cache_seqlens || !offsets || !counts)
+    return fail(MLA_ERR_INVALID, "null pointer");
+  if ((long long)batch * s_q > (1 << 24)) return fail(MLA_ERR_UNSUPPORTED, "batch * s_q too large");
+  if (num_pages * (long long)MLA_PAGE_BLOCK_SIZE * h_kv * MLA_D_QK * 2 > (long long)mla::kSparseMaxCacheBytes)
+    return fail(MLA_ERR_UNSUPPORTED, "the sparse decode addresses caches up to %u bytes", mla::kSparseMaxCacheBytes);
+  hipError_t e = mla::launch_sparse_prepare(indices, indptr, batch * s_q, s_q, block_table, max_blocks,
+                                            cache_seqlens, num_pages, h_kv, offsets, counts, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse prepare launch");
+  return ok();
+}
+
+int mla_sparse_decode(const void* q, const void* kcache, int64_t num_pages, const uint32_t* offsets,
+                      const int32_t* indptr, const int32_t* counts, int batch, int s_q, int h_q, int h_kv,
+                      int d_qk, int dv, int page_block_size, const int32_t* tile_metadata, int num_parts,
+                      const int32_t* num_splits, float softmax_scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (batch <= 0 || s_q <= 0) return fail(MLA_ERR_INVALID, "batch and s_q must be positive");
+  if ((long long)batch * s_q > MLA_MAX_BATCH)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * s_q query rows exceed MLA_MAX_BATCH (%d)", MLA_MAX_BATCH);
+  const SparseArgs sp{offsets, indptr};
+  // every query token is a sequence of its own: [batch * s_q, 1, h_q, ...] views of q, out and lse
+  return decode_common(kDecode | kCombine, 0, &sp, q, kcache, num_pages, nullptr, 0, counts, batch * s_q, 1, h_q,
+                       h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts, num_splits, 0, softmax_scale, out,
+                       lse, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

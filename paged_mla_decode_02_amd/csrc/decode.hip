@@ -331,6 +331,36 @@ __device__ __forceinline__ void dequant_slice(const LDS_AS char* src, LDS_AS cha
   for (int c = 0; c < 2; ++c) *(LDS_AS u32x4_t*)(dst + slice_off(t, 64 + 2 * g + c)) = rope[c];
 }
 
+// Token-sparse decode.  A wave's 16-token slice of page blk of sequence b is
+// rows sp_offs[sp_rowptr[b] + 64 blk + 16 w + t], t < 16 (byte offsets; the
+// array is padded by one page, so a last page's reads stay inside it).  The 16
+// offsets move into LDS with one 16-lane transfer (4 bytes per lane), counted
+// with the page transfers, and each lane then reads the offsets of its two
+// tokens: no registers hold a page's offsets while it is in flight.
+__device__ __forceinline__ void dma4(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"((unsigned)(size_t)dst), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void stage_offs(LDS_AS char* dst, i32x4_t offs_rsrc, int row0, int blk, int w, int lane) {
+  if (lane < kSlice) dma4(dst, offs_rsrc, (row0 + blk * kPage + w * kSlice + lane) * 4);
+}
+// per-lane transfer offsets of a gathered slice: the swizzle of
+// slice_dma_offsets with each token's row read from the staged list; tokens past
+// the sequence's kept keys read zeros
+__device__ __forceinline__ SliceDma gathered_dma(const LDS_AS char* staged, int valid, int kvh, int lane) {
+  SliceDma d;
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    const int t = 8 * th + (lane >> 3);
+    uint32_t off = *(const LDS_AS uint32_t*)(staged + 4 * t);
+    if (t >= valid) off = kSparseNone;
+    d.vbase[th] = (int)(off + (uint32_t)(kvh * kRowBytes) + (uint32_t)(((lane & 7) ^ swz(t)) << 4));
+  }
+  return d;
+}
+
 __device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh, int row, int& s,
                                            long long& qo) {
   s = row / p.group;
@@ -663,7 +693,8 @@ constexpr int kPsPbuf = 2 * kPageBytes;
 constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
 constexpr int kPsAbuf = kPsXmax + 2 * kPsRows * 4;
 constexpr int kPsSbuf = kPsAbuf + kPsRows * 4;
-constexpr int kPsLds = kPsSbuf + 2 * kPsRows * 2 * 4;
+constexpr int kPsOffs = kPsSbuf + 2 * kPsRows * 2 * 4;  // token-sparse: [2 page slots][4 waves][16] row offsets
+constexpr int kPsLds = kPsOffs + 2 * 4 * kSlice * 4;
 // transfer pieces of the next page issued during QK^T (the rest during PV)
 #ifndef MLA_QK_DMA
 #define MLA_QK_DMA 18
@@ -682,6 +713,7 @@ constexpr int kPvDma0 = kQkDma + kSmDma;
 // chunk on 16 different bank groups.
 __device__ __forceinline__ int pbuf_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
+template <bool kSparse>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_pairsplit(DecodeParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
@@ -735,6 +767,8 @@ decode_pairsplit(DecodeParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) paddr[rt][ks] = pbuf_off(rt * 32 + l32, 2 * ks + hb);
   const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+  i32x4_t offs_rsrc = {};
+  if constexpr (kSparse) offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);  // the row-offset list
 
   for (int b = i0; b <= j0; ++b) {
     const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
@@ -755,8 +789,26 @@ decode_pairsplit(DecodeParams p) {
     for (int dt = 0; dt < 4; ++dt) O[dt][0] = O[dt][1] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;  // l_run covers this wave's token group only
 
-    int ids = load_page_ids(p, b, sr.lo, lane);
-    if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+    // token-sparse: the sequence's rows are listed, not paged; the offsets of
+    // page blk + 1 are staged one page ahead (LDS slot by page parity)
+    i32x4_t grsrc = {};
+    if constexpr (kSparse) grsrc = make_rsrc(p.kcache, p.sp_cache_bytes);
+    const auto slice_valid = [&](int blk_) { return min(max(sr.L - blk_ * kPage - w * kSlice, 0), kSlice); };
+    LDS_AS char* offs_slot[2] = {smem + kPsOffs + w * 64, smem + kPsOffs + (4 + w) * 64};
+    int row0 = 0;
+    int ids = -1;
+    if constexpr (kSparse) {
+      row0 = ((const CONST_AS int32_t*)p.sp_rowptr)[b];
+      if (sr.lo < sr.hi) {
+        stage_offs(offs_slot[0], offs_rsrc, row0, sr.lo, w, lane);
+        if (sr.lo + 1 < sr.hi) stage_offs(offs_slot[1], offs_rsrc, row0, sr.lo + 1, w, lane);
+        wait_vmcnt<0>();
+        dma_slice(pages + w * kSliceBytes, grsrc, gathered_dma(offs_slot[0], slice_valid(sr.lo), kvh, lane));
+      }
+    } else {
+      ids = load_page_ids(p, b, sr.lo, lane);
+      if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+    }
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
       const int pb = (blk - sr.lo) & 1;
       wait_vmcnt<0>();
@@ -766,10 +818,18 @@ decode_pairsplit(DecodeParams p) {
       const bool has_next = blk + 1 < sr.hi;
       LDS_AS char* ndst = pages + (pb ^ 1) * kPageBytes + w * kSliceBytes;
       i32x4_t nrsrc = {0, 0, 0, 0};
+      SliceDma ndma = dma;
       if (has_next) {
-        const int k = (blk + 1 - sr.lo) & 63;
-        if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
-        nrsrc = page_rsrc(p, page_id(ids, k), blk + 1, sr.L);
+        if constexpr (kSparse) {
+          const int ns = (blk + 1 - sr.lo) & 1;
+          nrsrc = grsrc;
+          ndma = gathered_dma(offs_slot[ns], slice_valid(blk + 1), kvh, lane);
+          if (blk + 2 < sr.hi) stage_offs(offs_slot[ns ^ 1], offs_rsrc, row0, blk + 2, w, lane);
+        } else {
+          const int k = (blk + 1 - sr.lo) & 63;
+          if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
+          nrsrc = page_rsrc(p, page_id(ids, k), blk + 1, sr.L);
+        }
       }
       const LDS_AS char* page = pages + pb * kPageBytes;
 
@@ -796,7 +856,7 @@ decode_pairsplit(DecodeParams p) {
           if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if constexpr (decltype(with_dma)::value) {
 #pragma unroll
-            for (int i = ks * kQkDma / 36; i < (ks + 1) * kQkDma / 36; ++i) dma_piece(ndst, nrsrc, dma, i);
+            for (int i = ks * kQkDma / 36; i < (ks + 1) * kQkDma / 36; ++i) dma_piece(ndst, nrsrc, ndma, i);
           }
         }
         return S0 + S1;
@@ -836,7 +896,7 @@ decode_pairsplit(DecodeParams p) {
         ps += S[r];
         if (kSmDma > 0 && has_next && r % 4 == 3) {
           for (int i = kQkDma + (r / 4) * kSmDma / 4; i < kQkDma + (r / 4 + 1) * kSmDma / 4; ++i)
-            dma_piece(ndst, nrsrc, dma, i);
+            dma_piece(ndst, nrsrc, ndma, i);
         }
       }
       l_run += half_sum(ps);
@@ -900,7 +960,7 @@ decode_pairsplit(DecodeParams p) {
         if (has_next) {
           for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
                ++i)
-            dma_piece(ndst, nrsrc, dma, i);
+            dma_piece(ndst, nrsrc, ndma, i);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -966,12 +1026,13 @@ hipError_t launch_one(K kernel, int lds, const DecodeParams& p, hipStream_t stre
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  if (tile_rows_for(p.rows) == 16) {
+  if (tile_rows_for(p.rows) == 16 && !p.sparse) {
     if (p.kv_fp8) return launch_one(decode_tokensplit<true>, TsLayout<true>::kLds, p, stream);
     return launch_one(decode_tokensplit<false>, TsLayout<false>::kLds, p, stream);
   }
   if (p.kv_fp8) return hipErrorInvalidValue;  // the 64-row kernel reads bf16 pages only
-  return launch_one(decode_pairsplit, kPsLds, p, stream);
+  if (p.sparse) return launch_one(decode_pairsplit<true>, kPsLds, p, stream);
+  return launch_one(decode_pairsplit<false>, kPsLds, p, stream);
 }
 
 }  // namespace mla

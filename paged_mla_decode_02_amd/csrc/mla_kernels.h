@@ -48,7 +48,17 @@ struct DecodeParams {
   float scale_log2;          // softmax_scale * log2(e)
   int xcd_map;               // workgroup -> (part, row tile, kv head) mapping keeps a part on one XCD
   int kv_fp8;                // kcache rows are the 656-byte FP8 format (kF8RowBytes) instead of bf16
+  // token-sparse decode: sequence b of the launch is query row b of the caller;
+  // its keys are the cache rows at byte offsets sp_offs[sp_rowptr[b] + i],
+  // i < seqlens[b] (the kept entries of its index list)
+  const uint32_t* sp_offs;
+  const int32_t* sp_rowptr;
+  uint32_t sp_cache_bytes;
+  int sparse;
 };
+// byte offset that no cache holds: a transfer from it reads zeros
+constexpr uint32_t kSparseNone = 0xF0000000u;
+constexpr uint32_t kSparseMaxCacheBytes = 0xE0000000u;
 
 // Records the status of the last C-ABI call on this thread (message for
 // mla_last_error) and returns `code`.
@@ -66,6 +76,10 @@ hipError_t launch_kv_append(const uint16_t* new_kv, int batch, int s_new, int h_
 hipError_t launch_kv_append_fp8(const uint16_t* new_kv, int batch, int s_new, int h_kv, const int32_t* seqlens,
                                 const int32_t* block_table, int max_blocks, uint8_t* kcache, long long num_pages,
                                 int32_t* new_seqlens, hipStream_t stream);
+hipError_t launch_sparse_prepare(const int32_t* indices, const int32_t* indptr, int rows, int s_q,
+                                 const int32_t* block_table, int max_blocks, const int32_t* seqlens,
+                                 long long num_pages, int h_kv, uint32_t* offsets, int32_t* counts,
+                                 hipStream_t stream);
 hipError_t launch_unabsorb_out(const uint16_t* o_lat, const uint16_t* w_uv, int tokens, int h_q, uint16_t* out,
                                hipStream_t stream);
 

@@ -226,6 +226,35 @@ def make_fp8_cache(w: Workload, seed: int, scale_exp: int = -2) -> np.ndarray:
     return out.reshape(shape + (FP8_ROW_BYTES,))
 
 
+def make_sparse_indices(w: Workload, topk: int, seed: int, invalid: float = 0.0, shuffle: bool = False,
+                        empty_rows: Sequence[int] = ()):
+    """CSR selections for a token-sparse decode of workload w: (indices int32,
+    indptr int32 [b*s_q + 1]).
+
+    Row v = b*s_q + s lists min(topk, L_b) distinct positions drawn uniformly
+    from [0, L_b), ascending; with ``invalid`` > 0 about that fraction of extra
+    entries that address no cached token (-1, L_b, L_b + 63, past the table) is
+    added and the row is shuffled; ``shuffle`` shuffles every row; rows in
+    ``empty_rows`` list nothing.  Drawn from PCG64(seed + 7727)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 7727))
+    rows, ptr = [], [0]
+    for v in range(w.batch * w.s_q):
+        L = int(w.cache_seqlens[v // w.s_q])
+        if v in empty_rows or L <= 0:
+            sel = np.zeros(0, dtype=np.int64)
+        else:
+            sel = np.sort(rng.choice(L, size=min(topk, L), replace=False))
+        if invalid > 0:
+            n_bad = int(rng.binomial(max(len(sel), 1), invalid))
+            bad = rng.choice(np.array([-1, L, L + 63, w.max_blocks * PAGE + 5]), size=n_bad)
+            sel = rng.permutation(np.concatenate([sel, bad]))
+        elif shuffle:
+            sel = rng.permutation(sel)
+        rows.append(sel.astype(np.int32))
+        ptr.append(ptr[-1] + len(sel))
+    return np.concatenate(rows).astype(np.int32), np.array(ptr, dtype=np.int32)
+
+
 def permute_pages(w: Workload, seed: int) -> Workload:
     """Same logical cache with physical pages relabelled by a random permutation.
 
