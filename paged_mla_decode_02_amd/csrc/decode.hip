@@ -340,7 +340,7 @@ __device__ __forceinline__ void dequant_slice(const LDS_AS char* src, LDS_AS cha
 __device__ __forceinline__ void dma4(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :
-               : "s"((unsigned)(size_t)dst), "v"(voffset), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)dst)), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
 __device__ __forceinline__ void stage_offs(LDS_AS char* dst, i32x4_t offs_rsrc, int row0, int blk, int w, int lane) {
@@ -382,8 +382,9 @@ template <bool kFp8>
 struct TsLayout {
   static constexpr int kSlot = kFp8 ? kF8SliceBytes : kSliceBytes;
   static constexpr int kWave = kFp8 ? 2 * kF8SliceBytes + kSliceBytes : 2 * kSliceBytes;
-  static constexpr int kDma = kFp8 ? kF8SliceDma : kSliceDma;
-  static constexpr int kLds = 4 * kWave + 4 * 16 * 2 * 4;
+  static constexpr int kDma = kFp8 ? kF8SliceDma : kSliceDma;  // transfers per slice issue
+  static constexpr int kStat = 4 * kWave;                        // [4 waves][16 rows][m, l]
+  static constexpr int kLds = kStat + 4 * 16 * 2 * 4;
 };
 
 template <bool kFp8>
@@ -403,7 +404,7 @@ decode_tokensplit(DecodeParams p) {
 
   LDS_AS char* slices = smem + w * Lay::kWave;                     // transfer slot k at k * Lay::kSlot
   LDS_AS char* bslice = smem + w * Lay::kWave + 2 * kF8SliceBytes;  // FP8 only: dequantised slice
-  LDS_AS float* mstat = (LDS_AS float*)(smem + 4 * Lay::kWave);     // [4 waves][16 rows][2]
+  LDS_AS float* mstat = (LDS_AS float*)(smem + Lay::kStat);         // [4 waves][16 rows][2]
 
   // lane roles: QK output / PV operand B -> query row (lane & 15)
   const int r16 = lane & 15;
@@ -423,10 +424,11 @@ decode_tokensplit(DecodeParams p) {
   F8Dma f8dma;
   if constexpr (kFp8) f8dma = fp8_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
   else dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
-  // this wave's slice of page blk (physical id pid) of a sequence of length L
-  auto issue = [&](LDS_AS char* dst, int pid, int blk_, int L_) {
-    if constexpr (kFp8) dma_slice_fp8(dst, page_rsrc(p, pid, blk_, L_, kF8RowBytes), f8dma, lane);
-    else dma_slice(dst, page_rsrc(p, pid, blk_, L_), dma);
+  // this wave's slice of page blk of sequence range r, whose id is entry k of the
+  // block-table window `ids_` (entries r.lo .. r.lo + 63)
+  auto issue = [&](LDS_AS char* dst, int ids_, int k, int blk_, const SeqRange& r) {
+    if constexpr (kFp8) dma_slice_fp8(dst, page_rsrc(p, page_id(ids_, k), blk_, r.L, kF8RowBytes), f8dma, lane);
+    else dma_slice(dst, page_rsrc(p, page_id(ids_, k), blk_, r.L), dma);
   };
 
   // queries: B operand of the 16x16x32 QK MFMA, 8 dims per lane per k-step.
@@ -464,7 +466,7 @@ decode_tokensplit(DecodeParams p) {
     ids = load_page_ids(p, b, sr.lo, lane);
     vm_drain();
   }
-  if (sr.lo < sr.hi) issue(slices, page_id(ids, 0), sr.lo, sr.L);
+  if (sr.lo < sr.hi) issue(slices, ids, 0, sr.lo, sr);
   for (;;) {
     const bool has_next = b < j0;
     SeqDesc nd2 = {};
@@ -488,10 +490,10 @@ decode_tokensplit(DecodeParams p) {
       if (blk + 1 < sr.hi) {
         const int k = (blk + 1 - sr.lo) & 63;
         if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
-        issue(slices + (buf ^ 1) * Lay::kSlot, page_id(ids, k), blk + 1, sr.L);
+        issue(slices + (buf ^ 1) * Lay::kSlot, ids, k, blk + 1, sr);
         wait_vmcnt<Lay::kDma>();
       } else if (has_next && nr.lo < nr.hi) {
-        issue(slices + (buf ^ 1) * Lay::kSlot, page_id(nids, 0), nr.lo, nr.L);
+        issue(slices + (buf ^ 1) * Lay::kSlot, nids, 0, nr.lo, nr);
         next_started = true;
         wait_vmcnt<Lay::kDma>();
       } else {
@@ -593,31 +595,32 @@ decode_tokensplit(DecodeParams p) {
     // consumed (bf16) or the dequantised slice (FP8)
     const int dbuf = kFp8 ? 2 * kF8SliceBytes : (buf ^ 1) * kSliceBytes;
     wg_barrier();  // every wave is done with its slices
-    if (lane < 16) {
-      mstat[(w * 16 + lane) * 2 + 0] = m_run;
-      mstat[(w * 16 + lane) * 2 + 1] = l_run;
-    }
+    if (lane < 16) *(LDS_AS f32x2_t*)(mstat + (w * 16 + lane) * 2) = f32x2_t{m_run, l_run};
     wg_barrier();
-    {
-      float M = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) M = fmaxf(M, mstat[(v * 16 + r16) * 2]);
-      const float c_own = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) O[i] *= c_own;
-    }
-    // reducer lane mapping: row lane >> 2, 16 dims at (lane & 3) * 16 within a 64-dim slab
+    // reducer lane mapping: row lane >> 2, 16 dims at (lane & 3) * 16 within a
+    // 64-dim slab.  With M the largest of the four waves' maxima m_v, the row is
+    // sum_v 2^(m_v - M) O_v / sum_v 2^(m_v - M) l_v; the weight of each wave,
+    // divided by that sum, multiplies its O_v as it is summed (a wave that saw no
+    // key has m_v = -inf, O_v = 0, l_v = 0 and weight 0).
     const int rr = lane >> 2;
     const int rrow = mt * 16 + rr;
-    float M = -INFINITY, lsum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) M = fmaxf(M, mstat[(v * 16 + rr) * 2]);
+    float mv[4], lv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const float mv = mstat[(v * 16 + rr) * 2];
-      lsum += (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M) * mstat[(v * 16 + rr) * 2 + 1];
+      const f32x2_t st = *(const LDS_AS f32x2_t*)(mstat + (v * 16 + rr) * 2);
+      mv[v] = st[0];
+      lv[v] = st[1];
+    }
+    const float M = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));
+    float cv[4], lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      cv[v] = (mv[v] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv[v] - M);
+      lsum += cv[v] * lv[v];
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) cv[v] *= inv;
     int rs;
     long long ro;
     row_coords(p, b, kvh, rrow < p.rows ? rrow : 0, rs, ro);
@@ -631,25 +634,30 @@ decode_tokensplit(DecodeParams p) {
       for (int dt = 0; dt < 16; ++dt)
         *(LDS_AS f32x4_t*)(dump + r16 * kDumpStride + dt * 16 + grp * 4) = O[half * 16 + dt];
       wg_barrier();
-      f32x4_t acc[4] = {};
+      // all 16 reads in flight before the first sum
+      f32x4_t xs[4][4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const LDS_AS float* src = (const LDS_AS float*)(smem + v * Lay::kWave + dbuf);
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          acc[k] += *(const LDS_AS f32x4_t*)(src + rr * kDumpStride + w * 64 + (lane & 3) * 16 + k * 4);
+          xs[v][k] = *(const LDS_AS f32x4_t*)(src + rr * kDumpStride + w * 64 + (lane & 3) * 16 + k * 4);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      f32x4_t acc[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = cv[0] * xs[0][k] + cv[1] * xs[1][k] + cv[2] * xs[2][k] + cv[3] * xs[3][k];
       if (rrow < p.rows && sr.ok) {
         const int d0 = half * 256 + w * 64 + (lane & 3) * 16;
         if (split) {
           f32x4_t* dst = (f32x4_t*)(p.o_acc + slot_row * kDv + d0);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) dst[k] = acc[k] * inv;
+          for (int k = 0; k < 4; ++k) dst[k] = acc[k];
         } else {
           u32x4_t pk[2];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const f32x4_t v = acc[k] * inv;
+            const f32x4_t v = acc[k];
             pk[k >> 1][(k & 1) * 2 + 0] = pack_bf16(v[0], v[1]);
             pk[k >> 1][(k & 1) * 2 + 1] = pack_bf16(v[2], v[3]);
           }
@@ -674,7 +682,7 @@ decode_tokensplit(DecodeParams p) {
     ids = nids;
     nr = seq_range(p, nd2, b + 1, i0, f0, j0, e0, ord0);
     nids = nids2;
-    if (!next_started && sr.lo < sr.hi) issue(slices + buf * Lay::kSlot, page_id(ids, 0), sr.lo, sr.L);
+    if (!next_started && sr.lo < sr.hi) issue(slices + buf * Lay::kSlot, ids, 0, sr.lo, sr);
   }
 }
 
