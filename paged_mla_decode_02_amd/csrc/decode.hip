@@ -702,6 +702,11 @@ constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
 constexpr int kPsAbuf = kPsXmax + 2 * kPsRows * 4;
 constexpr int kPsSbuf = kPsAbuf + kPsRows * 4;
 constexpr int kPsOffs = kPsSbuf + 2 * kPsRows * 2 * 4;  // token-sparse: [2 page slots][4 waves][16] row offsets
+// chunk end: per wave, its 128 output dims of the 64 rows as [row][dim] fp32
+// (row stride 132 floats) plus the rows' output offsets, inside the page buffers
+constexpr int kPsStgStride = 132;
+constexpr int kPsStgBytes = kPsRows * kPsStgStride * 4 + kPsRows * 8;
+static_assert(4 * kPsStgBytes <= kPsPbuf, "the chunk-end staging must fit in the page buffers");
 constexpr int kPsLds = kPsOffs + 2 * 4 * kSlice * 4;
 // transfer pieces of the next page issued during QK^T (the rest during PV)
 #ifndef MLA_QK_DMA
@@ -979,9 +984,16 @@ decode_pairsplit(DecodeParams p) {
       sbuf[(tg * kPsRows + trow) * 2 + 0] = m_run;
       sbuf[(tg * kPsRows + trow) * 2 + 1] = l_run;
     }
-    wg_barrier();
+    wg_barrier();  // ... and every wave is done with the page buffers
     const bool split = sr.chunks > 1;
     const long long slot = (long long)(sr.base + sr.ord) * p.h_kv + kvh;
+    // Each wave writes its 128 normalised output dims of the 64 rows into its
+    // own region of the page buffers as [row][dim], with every row's output
+    // offset (elements; -1 for a row that is not stored), and then stores whole
+    // row segments: 512 B of fp32 partial per 32 lanes or 256 B of bf16 output
+    // per 16 lanes, instead of 16-byte pieces spread over 32 rows.
+    LDS_AS float* stg = (LDS_AS float*)(smem + w * kPsStgBytes);
+    LDS_AS long long* roff = (LDS_AS long long*)(smem + w * kPsStgBytes + kPsRows * kPsStgStride * 4);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int rl = rt * 32 + l32;
@@ -989,31 +1001,50 @@ decode_pairsplit(DecodeParams p) {
       const float mrow = sbuf[rl * 2 + 0];  // same reference in both token groups
       const float lrow = sbuf[rl * 2 + 1] + sbuf[(kPsRows + rl) * 2 + 1];
       const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-      if (orow < p.rows && sr.ok) {
-        int os;
-        long long oo;
-        row_coords(p, b, kvh, orow, os, oo);
-        const long long srow = slot * p.rows + orow;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int d0 = w * 128 + dt * 32 + 8 * j + 4 * hb;
-            f32x4_t v = {O[dt][rt][4 * j], O[dt][rt][4 * j + 1], O[dt][rt][4 * j + 2], O[dt][rt][4 * j + 3]};
-            v *= inv;
-            if (split) {
-              *(f32x4_t*)(p.o_acc + srow * kDv + d0) = v;
-            } else {
-              u32x2_t pk = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-              *(u32x2_t*)(p.out + oo * kDv + d0) = pk;
-            }
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t v = {O[dt][rt][4 * j], O[dt][rt][4 * j + 1], O[dt][rt][4 * j + 2], O[dt][rt][4 * j + 3]};
+          *(LDS_AS f32x4_t*)(stg + rl * kPsStgStride + dt * 32 + 8 * j + 4 * hb) = v * inv;
+        }
+      if (hb == 0) {
+        long long off = -1;
+        if (orow < p.rows && sr.ok) {
+          int os;
+          long long oo;
+          row_coords(p, b, kvh, orow, os, oo);
+          const long long srow = slot * p.rows + orow;
+          off = (split ? srow : oo) * kDv;
+          if (w == 0) {
+            const float l2 = lrow > 0.f ? mrow + __builtin_amdgcn_logf(lrow) : -INFINITY;
+            if (split) p.lse_acc[srow] = l2;
+            else p.lse[oo] = l2 * kLn2;
           }
         }
-        if (w == 0 && hb == 0) {
-          const float l2 = lrow > 0.f ? mrow + __builtin_amdgcn_logf(lrow) : -INFINITY;
-          if (split) p.lse_acc[srow] = l2;
-          else p.lse[oo] = l2 * kLn2;
-        }
+        roff[rl] = off;
+      }
+    }
+    // this wave's own LDS writes are visible to its later reads (in order)
+    if (split) {
+#pragma unroll 8
+      for (int i = 0; i < kPsRows / 2; ++i) {
+        const int r = 2 * i + (lane >> 5);
+        const long long off = roff[r];
+        const f32x4_t v = *(const LDS_AS f32x4_t*)(stg + r * kPsStgStride + 4 * (lane & 31));
+        if (off >= 0) *(f32x4_t*)(p.o_acc + off + w * 128 + 4 * (lane & 31)) = v;
+      }
+    } else {
+#pragma unroll 8
+      for (int i = 0; i < kPsRows / 4; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const long long off = roff[r];
+        const LDS_AS float* src = stg + r * kPsStgStride + 8 * (lane & 15);
+        const f32x4_t v0 = *(const LDS_AS f32x4_t*)src;
+        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(src + 4);
+        const u32x4_t pk = {pack_bf16(v0[0], v0[1]), pack_bf16(v0[2], v0[3]), pack_bf16(v1[0], v1[1]),
+                            pack_bf16(v1[2], v1[3])};
+        if (off >= 0) *(u32x4_t*)(p.out + off + w * 128 + 8 * (lane & 15)) = pk;
       }
     }
     wg_barrier();  // sbuf and page buffers are reused by the next sequence
