@@ -423,9 +423,6 @@ def main():
     cfg = workloads.CONFIGS[args.config]
     w = workloads.config_workload(args.config)
     fp8 = args.kv == "fp8"
-    if fp8 and w.rows > 16:
-        print("--kv fp8: the FP8 cache covers s_q * h_q / h_kv <= 16 (workloads 0 and 1)", file=sys.stderr)
-        sys.exit(2)
     bytes_step, flops_step, kv_bytes = algorithmic(w, mla.FP8_ROW_BYTES if fp8 else 576 * 2)
 
     # inputs resident in HBM; enough cache copies to defeat the MALL

@@ -242,9 +242,9 @@ int mla_kv_append(const void* new_kv, int batch, int s_new, int h_kv, const int3
  *   unspecified bytes.  Same errors as mla_kv_append.
  * mla_decode_paged_fp8, mla_decode_splitkv_fp8: as mla_decode_paged and
  *   mla_decode_splitkv with kcache_fp8 in that format (the metadata, workspace
- *   and the combine stage, mla_combine_splits, are the same); for
- *   s_q * h_q / h_kv <= 16 (one 16-row tile per KV head), else
- *   MLA_ERR_UNSUPPORTED.
+ *   and the combine stage, mla_combine_splits, are the same), for any
+ *   s_q * h_q / h_kv; the pages are dequantised in the kernels, never written
+ *   back.
  */
 int mla_kv_append_fp8(const void* new_kv, int batch, int s_new, int h_kv, const int32_t* cache_seqlens,
                       const int32_t* block_table, int max_blocks, void* kcache_fp8, int64_t num_pages,

@@ -143,8 +143,6 @@ int decode_common(int stages, int kv_fp8, const SparseArgs* sp, const void* q, c
     return fail(MLA_ERR_INVALID, "q, kcache and out must be 16-byte aligned");
   if ((long long)page_block_size * h_kv * (kv_fp8 ? MLA_FP8_ROW_BYTES : MLA_D_QK * 2) > 0xffffffffLL)
     return fail(MLA_ERR_UNSUPPORTED, "page too large for 32-bit offsets");
-  if (kv_fp8 && mla::tile_rows_for(rows) != 16)
-    return fail(MLA_ERR_UNSUPPORTED, "the FP8 cache supports s_q * h_q / h_kv <= 16 (got %d)", rows);
   const size_t need = (size_t)(batch + num_parts) * (size_t)h_kv * (size_t)rows * (size_t)(dv + 1) * 4u;
   if (!workspace || workspace_bytes < need)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,

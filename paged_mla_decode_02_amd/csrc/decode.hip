@@ -726,9 +726,56 @@ constexpr int kPvDma0 = kQkDma + kSmDma;
 // chunk on 16 different bank groups.
 __device__ __forceinline__ int pbuf_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-template <bool kSparse>
+// FP8 pages in the 64-row kernel.  A page lives in LDS as its 64 token-major
+// 656-byte rows: 41 transfers of 1 KB, wave w issuing transfers w, w + 4, ...
+// Rows 656 bytes apart put 16 consecutive tokens on 16 distinct 16-byte bank
+// groups, so the K operand reads (16 bytes of one token per lane) and the
+// transposed V reads are conflict free without a swizzle.
+constexpr int kF8PageBytes = kPage * kF8RowBytes;  // 41984
+constexpr int kF8PageDma = kF8PageBytes / 1024;     // 41
+constexpr int kF8WaveDma = (kF8PageDma + 3) / 4;    // 11 (waves 1-3 issue 10)
+static_assert(kF8PageBytes % 1024 == 0, "an FP8 page is a whole number of transfers");
+struct PageDmaF8 {
+  int off[kF8WaveDma];
+};
+__device__ __forceinline__ PageDmaF8 fp8_page_dma_offsets(int w, int kvh, int h_kv, int lane) {
+  PageDmaF8 d;
+#pragma unroll
+  for (int i = 0; i < kF8WaveDma; ++i) {
+    const int o = 1024 * (w + 4 * i) + 16 * lane;  // byte of the LDS page image
+    const int t = o / kF8RowBytes;                 // its token and byte within the row
+    d.off[i] = (t * h_kv + kvh) * kF8RowBytes + (o - t * kF8RowBytes);
+  }
+  return d;
+}
+// transfer i of wave w's share of an FP8 page
+__device__ __forceinline__ void dma_piece_f8(LDS_AS char* page, i32x4_t rsrc, const PageDmaF8& d, int w, int i) {
+  if (w + 4 * i < kF8PageDma) dma16(page + 1024 * (w + 4 * i), rsrc, d.off[i]);
+}
+// 8 e4m3 codes (two words) -> 8 bf16 times a power-of-two scale (exact)
+__device__ __forceinline__ bf16x8_t cvt8_fp8(unsigned w0, unsigned w1, float sc) {
+  const u32x4_t r = {cvt_fp8x2(w0, sc, false), cvt_fp8x2(w0, sc, true), cvt_fp8x2(w1, sc, false),
+                     cvt_fp8x2(w1, sc, true)};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+// 8 bf16 values, element j times sc[j] (powers of two: exact while the
+// products stay in bf16's normal range)
+__device__ __forceinline__ bf16x8_t scale8(bf16x8_t v, const float* sc) {
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_bf16(__builtin_bit_cast(float, u[i] << 16) * sc[2 * i],
+                     __builtin_bit_cast(float, u[i] & 0xffff0000u) * sc[2 * i + 1]);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+
+template <bool kSparse, bool kFp8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_pairsplit(DecodeParams p) {
+  static_assert(!(kSparse && kFp8), "the token-sparse decode reads bf16 rows");
+  constexpr int kPg = kFp8 ? kF8PageBytes : kPageBytes;  // LDS bytes of one page
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
   LDS_AS char* pages = smem;
@@ -780,6 +827,17 @@ decode_pairsplit(DecodeParams p) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) paddr[rt][ks] = pbuf_off(rt * 32 + l32, 2 * ks + hb);
   const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
+  // FP8 pages: the K operand row of this lane's token; the transposed V read of
+  // lanes 2k, 2k+1 of a 16-lane group addresses token k of the group's 8 at
+  // bytes +0 / +8, so that lane i receives dim i of 8 consecutive tokens
+  // (16 tokens per k-step: 8 * hb + k16 / 2; dims 128 w + 32 dt + 16 (g16 & 1) + k16)
+  int frow = 0, vaddr8 = 0;
+  PageDmaF8 fdma = {};
+  if constexpr (kFp8) {
+    frow = (32 * tg + l32) * kF8RowBytes;
+    vaddr8 = (8 * hb + (k16 >> 1)) * kF8RowBytes + 128 * w + 16 * (g16 & 1) + 8 * (k16 & 1);
+    fdma = fp8_page_dma_offsets(w, kvh, p.h_kv, lane);
+  }
   i32x4_t offs_rsrc = {};
   if constexpr (kSparse) offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);  // the row-offset list
 
@@ -791,11 +849,14 @@ decode_pairsplit(DecodeParams p) {
     const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
 
     // rows past the last one compute on row 0's query and are never stored
+    // (FP8 pages: k-steps 2j, 2j+1 of the latent take bytes 0-7 / 8-15 of the
+    // 16-byte chunk 32 j + 16 hb, i.e. dims 32 j + 16 hb + 8 (ks & 1) .. +7)
     bf16x8_t qreg[36];
     {
-      const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk) + hb;
+      const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk);
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks) qreg[ks] = qp[ks * 2];
+      for (int ks = 0; ks < 36; ++ks)
+        qreg[ks] = qp[kFp8 && ks < 32 ? 4 * (ks >> 1) + 2 * hb + (ks & 1) : 2 * ks + hb];
     }
     f32x16_t O[4][2];
 #pragma unroll
@@ -820,7 +881,15 @@ decode_pairsplit(DecodeParams p) {
       }
     } else {
       ids = load_page_ids(p, b, sr.lo, lane);
-      if (sr.lo < sr.hi) dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+      if (sr.lo < sr.hi) {
+        if constexpr (kFp8) {
+          const i32x4_t r = page_rsrc(p, page_id(ids, 0), sr.lo, sr.L, kF8RowBytes);
+#pragma unroll
+          for (int i = 0; i < kF8WaveDma; ++i) dma_piece_f8(pages, r, fdma, w, i);
+        } else {
+          dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
+        }
+      }
     }
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
       const int pb = (blk - sr.lo) & 1;
@@ -829,7 +898,8 @@ decode_pairsplit(DecodeParams p) {
       // the next page's slice moves in pieces spread over this page's MFMAs:
       // kQkDma pieces during QK^T, the rest during PV
       const bool has_next = blk + 1 < sr.hi;
-      LDS_AS char* ndst = pages + (pb ^ 1) * kPageBytes + w * kSliceBytes;
+      LDS_AS char* npage = pages + (pb ^ 1) * kPg;
+      LDS_AS char* ndst = npage + w * kSliceBytes;
       i32x4_t nrsrc = {0, 0, 0, 0};
       SliceDma ndma = dma;
       if (has_next) {
@@ -841,10 +911,10 @@ decode_pairsplit(DecodeParams p) {
         } else {
           const int k = (blk + 1 - sr.lo) & 63;
           if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
-          nrsrc = page_rsrc(p, page_id(ids, k), blk + 1, sr.L);
+          nrsrc = page_rsrc(p, page_id(ids, k), blk + 1, sr.L, kFp8 ? kF8RowBytes : kRowBytes);
         }
       }
-      const LDS_AS char* page = pages + pb * kPageBytes;
+      const LDS_AS char* page = pages + pb * kPg;
 
       // ---- S^T[32 tokens x 32 rows] = K . Q^T, two accumulation chains,
       // K operands fetched kAhead k-steps ahead.  The loop is instantiated with
@@ -874,9 +944,48 @@ decode_pairsplit(DecodeParams p) {
         }
         return S0 + S1;
       };
+      // FP8 pages: 20 operand reads per lane -- 16 latent chunks of 16 bytes (two
+      // k-steps each, dequantised with the token's group scale) and 4 rope
+      // k-steps of bf16 -- and the next page's kF8WaveDma transfers spread over them
+      auto qk8 = [&](auto with_dma) {
+        f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
+        const LDS_AS char* krow = page + frow;
+        const f32x4_t sc = *(const LDS_AS f32x4_t*)(krow + kLatent);  // the token's 4 group scales
+        auto rd = [&](int r) {
+          return *(const LDS_AS u32x4_t*)(krow + (r < 16 ? 32 * r + 16 * hb : kLatent + 16 + 32 * (r - 16) + 16 * hb));
+        };
+        constexpr int kAheadR = 3;  // operand reads in flight ahead of their MFMAs
+        u32x4_t kr[kAheadR + 1];
+#pragma unroll
+        for (int i = 0; i < kAheadR; ++i) kr[i] = rd(i);
+#pragma unroll
+        for (int r = 0; r < 20; ++r) {
+          if (r + kAheadR < 20) kr[(r + kAheadR) % (kAheadR + 1)] = rd(r + kAheadR);
+          const u32x4_t c = kr[r % (kAheadR + 1)];
+          if (r < 16) {
+            const float s8 = sc[r >> 2];
+            S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8_fp8(c[0], c[1], s8), qreg[2 * r], S0, 0, 0, 0);
+            S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8_fp8(c[2], c[3], s8), qreg[2 * r + 1], S1, 0, 0, 0);
+          } else {
+            const int ks = 32 + (r - 16);
+            if (ks & 1) S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c), qreg[ks], S1, 0, 0, 0);
+            else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c), qreg[ks], S0, 0, 0, 0);
+          }
+          if constexpr (decltype(with_dma)::value) {
+#pragma unroll
+            for (int i = r * kF8WaveDma / 20; i < (r + 1) * kF8WaveDma / 20; ++i) dma_piece_f8(npage, nrsrc, fdma, w, i);
+          }
+        }
+        return S0 + S1;
+      };
       f32x16_t S;
-      if (has_next) S = qk(std::true_type{});
-      else S = qk(std::false_type{});
+      if constexpr (kFp8) {
+        if (has_next) S = qk8(std::true_type{});
+        else S = qk8(std::false_type{});
+      } else {
+        if (has_next) S = qk(std::true_type{});
+        else S = qk(std::false_type{});
+      }
       __builtin_amdgcn_sched_barrier(0);
       // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page.
       // Scores stay unscaled (the scale is positive, so the max commutes with
@@ -907,7 +1016,7 @@ decode_pairsplit(DecodeParams p) {
       for (int r = 0; r < 16; ++r) {
         S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -m_use));
         ps += S[r];
-        if (kSmDma > 0 && has_next && r % 4 == 3) {
+        if (!kFp8 && kSmDma > 0 && has_next && r % 4 == 3) {
           for (int i = kQkDma + (r / 4) * kSmDma / 4; i < kQkDma + (r / 4 + 1) * kSmDma / 4; ++i)
             dma_piece(ndst, nrsrc, ndma, i);
         }
@@ -933,50 +1042,83 @@ decode_pairsplit(DecodeParams p) {
           }
         }
       }
-      // operands of k-step ks (16 tokens): P^T for both row tiles and V^T for the
-      // four 32-dim tiles; the next k-step's operands load while this one's
-      // MFMAs run
-      struct PvOps {
-        bf16x8_t bp[2];
-        bf16x8_t va[4];
-      };
-      auto load_ops = [&](int ks) {
-        PvOps o;
-        o.bp[0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
-        o.bp[1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
-        const LDS_AS char* vs = page + ks * kSliceBytes;
+      if constexpr (kFp8) {
+        // FP8 pages: V^T through the 8-bit transposed read, dequantised without
+        // scale; wave w's 128 dims are exactly latent group w, so each token's
+        // group-w scale multiplies its P^T entries instead
+        bf16x8_t bp[4][2];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int go = (dt >> 1) * kGroupBytes;
-          const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
-          const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
-          o.va[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        for (int ks = 0; ks < 4; ++ks) {
+          bp[ks][0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
+          bp[ks][1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
         }
-        return o;
-      };
-      PvOps ops[2];
-      ops[0] = load_ops(0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
-          ops[(ks + 1) & 1] = load_ops(ks + 1);
-          __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
-        }
-        const PvOps& o = ops[ks & 1];
+        for (int ks = 0; ks < 4; ++ks) {
+          float sv[8];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
-          O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
+          for (int j = 0; j < 8; ++j)
+            sv[j] = *(const LDS_AS float*)(page + (16 * ks + 8 * hb + j) * kF8RowBytes + kLatent + 4 * w);
+          bf16x8_t va[4];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (LDS_AS i32x2_t*)(page + 16 * ks * kF8RowBytes + 32 * dt + vaddr8));
+            va[dt] = cvt8_fp8((unsigned)v[0], (unsigned)v[1], 1.0f);
+          }
+          const bf16x8_t b0 = scale8(bp[ks][0], sv), b1 = scale8(bp[ks][1], sv);
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], b0, O[dt][0], 0, 0, 0);
+            O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], b1, O[dt][1], 0, 0, 0);
+          }
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-        if (has_next) {
-          for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
-               ++i)
-            dma_piece(ndst, nrsrc, ndma, i);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        // operands of k-step ks (16 tokens): P^T for both row tiles and V^T for the
+        // four 32-dim tiles; the next k-step's operands load while this one's
+        // MFMAs run
+        struct PvOps {
+          bf16x8_t bp[2];
+          bf16x8_t va[4];
+        };
+        auto load_ops = [&](int ks) {
+          PvOps o;
+          o.bp[0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
+          o.bp[1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
+          const LDS_AS char* vs = page + ks * kSliceBytes;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int go = (dt >> 1) * kGroupBytes;
+            const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
+            const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
+            o.va[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
+          return o;
+        };
+        PvOps ops[2];
+        ops[0] = load_ops(0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if (ks + 1 < 4) {
+            ops[(ks + 1) & 1] = load_ops(ks + 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+          }
+          const PvOps& o = ops[ks & 1];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
+            O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          if (has_next) {
+            for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
+                 ++i)
+              dma_piece(ndst, nrsrc, ndma, i);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- epilogue: (m, l) of both token groups for every row
@@ -1069,9 +1211,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     if (p.kv_fp8) return launch_one(decode_tokensplit<true>, TsLayout<true>::kLds, p, stream);
     return launch_one(decode_tokensplit<false>, TsLayout<false>::kLds, p, stream);
   }
-  if (p.kv_fp8) return hipErrorInvalidValue;  // the 64-row kernel reads bf16 pages only
-  if (p.sparse) return launch_one(decode_pairsplit<true>, kPsLds, p, stream);
-  return launch_one(decode_pairsplit<false>, kPsLds, p, stream);
+  if (p.kv_fp8) return launch_one(decode_pairsplit<false, true>, kPsLds, p, stream);
+  if (p.sparse) return launch_one(decode_pairsplit<true, false>, kPsLds, p, stream);
+  return launch_one(decode_pairsplit<false, false>, kPsLds, p, stream);
 }
 
 }  // namespace mla

@@ -8,6 +8,8 @@
   scales make that exact): out rel-L2 <= 1e-2, lse abs <= 1e-3, as for bf16.
 The FP8 caches are drawn directly in the format (workloads.make_fp8_cache), and
 slots past a sequence's end hold NaN codes, which must never reach a result.
+Both decode kernels are covered: up to 16 rows per KV head (token-split) and
+64-row tiles (pair-split), with scales from 2^-13 to 2^13.
 """
 import dataclasses
 
@@ -100,12 +102,43 @@ def test_decode_fp8_full_size_sampled(env):
     check(go[sel], gl[sel], ro, rl, "memory_bound_varlen fp8")
 
 
-def test_fp8_rejects_64_row_tiles(env):
-    torch, mla, _, _, _, dev = env
-    w = make_workload([64], s_q=1, h_q=64, seed=2)
-    with pytest.raises(mla.MlaError) as e:
-        decode_fp8(env, w, workloads.make_fp8_cache(w, seed=2))
-    assert e.value.code == -2
+@pytest.mark.parametrize("lens,s_q,h_q,h_kv,causal,parts,sexp", [
+    ([218, 164], 1, 64, 1, False, None, -2),     # one 64-row tile per KV head
+    ([1, 70, 300], 2, 64, 1, True, None, -2),    # 128 rows: two row tiles, causal
+    ([0, 129, 64], 1, 128, 2, False, None, 12),  # h_kv = 2, an empty sequence, large scales
+    ([1000, 3, 577], 1, 128, 1, False, 7, -12),  # forced splits (fp32 partials), small scales
+    ([333, 65], 1, 40, 1, False, None, -2),      # a ragged 40-row tile
+])
+def test_decode_fp8_64row_tiles(env, lens, s_q, h_q, h_kv, causal, parts, sexp):
+    """More than 16 rows per KV head: the 64-row kernel on FP8 pages.  The
+    softmax scale is divided by the cache scales' offset from the default, so
+    scores keep their usual size (an lse near 1e5 would be beyond fp32's 1e-3
+    absolute resolution) while V carries scales from 2^-13 to 2^13."""
+    _, _, orc, fp8, _, _ = env
+    w = make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal, seed=sum(lens) + h_q,
+                      scale=workloads.SCALE * 2.0 ** (-2 - sexp))
+    kc8 = poison_tails(w, workloads.make_fp8_cache(w, seed=len(lens) + 40, scale_exp=sexp))
+    go, gl = decode_fp8(env, w, kc8, num_parts=parts)
+    clean = kc8.copy()
+    lat = clean[..., :512]
+    lat[lat == 0x7F] = 0
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(clean)))
+    check(go, gl, ro, rl, f"{lens} rows {s_q * h_q // h_kv}")
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_decode_fp8_64row_full_size_sampled(env, cfg):
+    """compute_bound_full_heads (128 rows) and long_context (64 rows, ~32 splits
+    per sequence) over FP8 caches of their full size, on sampled rows."""
+    _, _, orc, fp8, _, _ = env
+    w = workloads.config_workload(cfg)
+    kc8 = workloads.make_fp8_cache(w, seed=cfg)
+    go, gl = decode_fp8(env, w, kc8)
+    rng = np.random.default_rng(cfg + 11)
+    n = w.batch * w.s_q * w.h_q
+    sel = np.sort(rng.choice(n, size=32, replace=False))
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(kc8)), sel=sel)
+    check(go[sel], gl[sel], ro, rl, f"config {cfg} fp8")
 
 
 @pytest.mark.parametrize("lens,s_new,h_kv", [([0, 1, 63, 64, 130], 1, 1), ([5, 62, 200], 3, 2),
