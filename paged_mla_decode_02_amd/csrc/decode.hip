@@ -707,7 +707,8 @@ constexpr int kPsOffs = kPsSbuf + 2 * kPsRows * 2 * 4;  // token-sparse: [2 page
 constexpr int kPsStgStride = 132;
 constexpr int kPsStgBytes = kPsRows * kPsStgStride * 4 + kPsRows * 8;
 static_assert(4 * kPsStgBytes <= kPsPbuf, "the chunk-end staging must fit in the page buffers");
-constexpr int kPsLds = kPsOffs + 2 * 4 * kSlice * 4;
+constexpr int kPsScl = kPsOffs + 2 * 4 * kSlice * 4;    // FP8 pages: [4 groups][64 tokens] fp32 scales of the page
+constexpr int kPsLds = kPsScl + 4 * kPage * 4;
 // transfer pieces of the next page issued during QK^T (the rest during PV)
 #ifndef MLA_QK_DMA
 #define MLA_QK_DMA 18
@@ -783,6 +784,7 @@ decode_pairsplit(DecodeParams p) {
   LDS_AS float* xmax = (LDS_AS float*)(smem + kPsXmax);  // [2 token groups][64 rows]
   LDS_AS float* abuf = (LDS_AS float*)(smem + kPsAbuf);  // [64 rows]
   LDS_AS float* sbuf = (LDS_AS float*)(smem + kPsSbuf);  // [2 token groups][64 rows][2]
+  LDS_AS float* scl = (LDS_AS float*)(smem + kPsScl);    // FP8 pages: [4 groups][64 tokens]
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -951,6 +953,10 @@ decode_pairsplit(DecodeParams p) {
         f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
         const LDS_AS char* krow = page + frow;
         const f32x4_t sc = *(const LDS_AS f32x4_t*)(krow + kLatent);  // the token's 4 group scales
+        if (rg == 0 && hb == 0) {  // waves 0 and 2 hold every token once: the PV waves' table
+#pragma unroll
+          for (int g = 0; g < 4; ++g) scl[g * kPage + 32 * tg + l32] = sc[g];
+        }
         auto rd = [&](int r) {
           return *(const LDS_AS u32x4_t*)(krow + (r < 16 ? 32 * r + 16 * hb : kLatent + 16 + 32 * (r - 16) + 16 * hb));
         };
@@ -1045,32 +1051,46 @@ decode_pairsplit(DecodeParams p) {
       if constexpr (kFp8) {
         // FP8 pages: V^T through the 8-bit transposed read, dequantised without
         // scale; wave w's 128 dims are exactly latent group w, so each token's
-        // group-w scale multiplies its P^T entries instead
+        // group-w scale multiplies its P^T entries instead.  The operands of
+        // k-step ks + 1 are read and converted while the MFMAs of k-step ks run.
+        const LDS_AS float* sclw = scl + w * kPage + 8 * hb;
         bf16x8_t bp[4][2];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           bp[ks][0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
           bp[ks][1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
         }
+        i32x2_t vr[2][4];
+        f32x4_t sr[2][2];
+        auto read_ops = [&](int ks, int slot) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            vr[slot][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (LDS_AS i32x2_t*)(page + 16 * ks * kF8RowBytes + 32 * dt + vaddr8));
+          sr[slot][0] = *(const LDS_AS f32x4_t*)(sclw + 16 * ks);
+          sr[slot][1] = *(const LDS_AS f32x4_t*)(sclw + 16 * ks + 4);
+        };
+        bf16x8_t va[2][4], bs[2][2];
+        auto convert_ops = [&](int ks, int slot) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) va[slot][dt] = cvt8_fp8((unsigned)vr[slot][dt][0], (unsigned)vr[slot][dt][1], 1.0f);
+          const float sv[8] = {sr[slot][0][0], sr[slot][0][1], sr[slot][0][2], sr[slot][0][3],
+                               sr[slot][1][0], sr[slot][1][1], sr[slot][1][2], sr[slot][1][3]};
+          bs[slot][0] = scale8(bp[ks][0], sv);
+          bs[slot][1] = scale8(bp[ks][1], sv);
+        };
+        read_ops(0, 0);
+        convert_ops(0, 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          float sv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            sv[j] = *(const LDS_AS float*)(page + (16 * ks + 8 * hb + j) * kF8RowBytes + kLatent + 4 * w);
-          bf16x8_t va[4];
+          const int cur = ks & 1;
+          if (ks + 1 < 4) read_ops(ks + 1, cur ^ 1);
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt) {
-            const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (LDS_AS i32x2_t*)(page + 16 * ks * kF8RowBytes + 32 * dt + vaddr8));
-            va[dt] = cvt8_fp8((unsigned)v[0], (unsigned)v[1], 1.0f);
+            O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cur][dt], bs[cur][0], O[dt][0], 0, 0, 0);
+            O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cur][dt], bs[cur][1], O[dt][1], 0, 0, 0);
           }
-          const bf16x8_t b0 = scale8(bp[ks][0], sv), b1 = scale8(bp[ks][1], sv);
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], b0, O[dt][0], 0, 0, 0);
-            O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], b1, O[dt][1], 0, 0, 0);
-          }
+          if (ks + 1 < 4) convert_ops(ks + 1, cur ^ 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
