@@ -373,7 +373,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
-                    help="cache format of the decode step (fp8: the 656-byte FP8 rows, <= 16 rows per KV head)")
+                    help="cache format of the decode step (fp8: the 656-byte FP8 rows)")
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="--op append: rows appended per sequence (default: the workload's s_q)")
     ap.add_argument("--topk", type=int, default=2048, help="--op sparse: entries selected per query")

@@ -236,7 +236,7 @@ def mla_decode_paged_fp8(q: torch.Tensor, kcache_fp8: torch.Tensor, block_table:
                          num_splits: torch.Tensor, causal: bool, softmax_scale: float,
                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None):
-    """Paged decode over the FP8 cache (uint8 [pages, 64, h_kv, 656]); rows <= 16."""
+    """Paged decode over the FP8 cache (uint8 [pages, 64, h_kv, 656]), any rows per KV head."""
     return _decode_call(_lib.mla_decode_paged_fp8, q, kcache_fp8, block_table, cache_seqlens, dv, tile_metadata,
                         num_splits, causal, softmax_scale, out, lse, workspace, fp8=True)
 

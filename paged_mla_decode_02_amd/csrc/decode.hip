@@ -40,6 +40,9 @@
 //     resident in registers), P goes through LDS, and PV is split by output dims
 //     (128 per wave), so each V element of a page is read from LDS once per
 //     workgroup.
+// Both also run on the FP8 cache (656-byte rows, see kF8RowBytes): the 16-row
+// kernel dequantises each slice in LDS, the 64-row kernel keeps FP8 pages in
+// LDS and dequantises its MFMA operands in registers.
 #include <type_traits>
 #include <utility>
 
