@@ -506,7 +506,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)}
-    traffic = None if fp8 else traffic_from_profiles(cfg["name"], "decode")
+    traffic = traffic_from_profiles(cfg["name"], "decode_fp8" if fp8 else "decode")
     roof["traffic"] = traffic
     roof["kernel"] = "decode (mla_decode_splitkv_fp8)" if fp8 else "decode (mla_decode_splitkv)"
     roof["launch_ms"] = round(float(dec_ms), 5)
