@@ -600,12 +600,15 @@ decode_tokensplit(DecodeParams p) {
     wg_barrier();  // every wave is done with its slices
     if (lane < 16) *(LDS_AS f32x2_t*)(mstat + (w * 16 + lane) * 2) = f32x2_t{m_run, l_run};
     wg_barrier();
-    // reducer lane mapping: row lane >> 2, 16 dims at (lane & 3) * 16 within a
-    // 64-dim slab.  With M the largest of the four waves' maxima m_v, the row is
-    // sum_v 2^(m_v - M) O_v / sum_v 2^(m_v - M) l_v; the weight of each wave,
-    // divided by that sum, multiplies its O_v as it is summed (a wave that saw no
-    // key has m_v = -inf, O_v = 0, l_v = 0 and weight 0).
-    const int rr = lane >> 2;
+    // Each wave produces the 64-dim slab 64 w .. 64 w + 63 of each half of the
+    // output rows, in the MFMA layout itself (row r16, dims 16 dt + 4 grp .. +3,
+    // dim tiles 4 w .. 4 w + 3): its own contribution stays in registers and
+    // only the three other waves' values go through LDS.  With M the largest of
+    // the four waves' maxima m_v, a row is sum_v 2^(m_v - M) O_v / sum_v
+    // 2^(m_v - M) l_v; each wave's weight, divided by that sum, multiplies its
+    // O_v as it is summed (a wave that saw no key has m_v = -inf, O_v = 0,
+    // l_v = 0 and weight 0).
+    const int rr = r16;
     const int rrow = mt * 16 + rr;
     float mv[4], lv[4];
 #pragma unroll
@@ -630,48 +633,54 @@ decode_tokensplit(DecodeParams p) {
     const bool split = sr.chunks > 1;
     const long long slot_row = ((long long)(sr.base + sr.ord) * p.h_kv + kvh) * p.rows + rrow;
     constexpr int kDumpStride = 260;  // floats per row: 256 + 4 pad
+    // the merge for wave index W (a compile-time constant: no dynamic indexing of O)
+    auto merge = [&](auto W) {
+      constexpr int kW = decltype(W)::value;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      LDS_AS float* dump = (LDS_AS float*)(smem + w * Lay::kWave + dbuf);
+      for (int half = 0; half < 2; ++half) {
+        LDS_AS float* dump = (LDS_AS float*)(smem + kW * Lay::kWave + dbuf);
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt)
-        *(LDS_AS f32x4_t*)(dump + r16 * kDumpStride + dt * 16 + grp * 4) = O[half * 16 + dt];
-      wg_barrier();
-      // all 16 reads in flight before the first sum
-      f32x4_t xs[4][4];
+        for (int dt = 0; dt < 16; ++dt)
+          if (dt / 4 != kW) *(LDS_AS f32x4_t*)(dump + r16 * kDumpStride + dt * 16 + grp * 4) = O[half * 16 + dt];
+        wg_barrier();
+        // the other waves' 12 reads in flight before the first sum
+        f32x4_t xs[3][4];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const LDS_AS float* src = (const LDS_AS float*)(smem + v * Lay::kWave + dbuf);
+        for (int j = 0; j < 3; ++j) {
+          const int v = (kW + 1 + j) & 3;
+          const LDS_AS float* src = (const LDS_AS float*)(smem + v * Lay::kWave + dbuf);
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            xs[j][k] = *(const LDS_AS f32x4_t*)(src + r16 * kDumpStride + (4 * kW + k) * 16 + grp * 4);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+        f32x4_t acc[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          xs[v][k] = *(const LDS_AS f32x4_t*)(src + rr * kDumpStride + w * 64 + (lane & 3) * 16 + k * 4);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-      f32x4_t acc[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] = cv[0] * xs[0][k] + cv[1] * xs[1][k] + cv[2] * xs[2][k] + cv[3] * xs[3][k];
-      if (rrow < p.rows && sr.ok) {
-        const int d0 = half * 256 + w * 64 + (lane & 3) * 16;
-        if (split) {
-          f32x4_t* dst = (f32x4_t*)(p.o_acc + slot_row * kDv + d0);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) dst[k] = acc[k];
-        } else {
-          u32x4_t pk[2];
+          acc[k] = cv[kW] * O[half * 16 + 4 * kW + k] + cv[(kW + 1) & 3] * xs[0][k] +
+                   cv[(kW + 2) & 3] * xs[1][k] + cv[(kW + 3) & 3] * xs[2][k];
+        if (rrow < p.rows && sr.ok) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const f32x4_t v = acc[k];
-            pk[k >> 1][(k & 1) * 2 + 0] = pack_bf16(v[0], v[1]);
-            pk[k >> 1][(k & 1) * 2 + 1] = pack_bf16(v[2], v[3]);
+            const int d0 = half * 256 + (4 * kW + k) * 16 + grp * 4;
+            if (split) {
+              *(f32x4_t*)(p.o_acc + slot_row * kDv + d0) = acc[k];
+            } else {
+              const u32x2_t pk = {pack_bf16(acc[k][0], acc[k][1]), pack_bf16(acc[k][2], acc[k][3])};
+              *(u32x2_t*)(p.out + ro * kDv + d0) = pk;
+            }
           }
-          u32x4_t* dst = (u32x4_t*)(p.out + ro * kDv + d0);
-          dst[0] = pk[0];
-          dst[1] = pk[1];
         }
+        wg_barrier();
       }
-      wg_barrier();
+    };
+    switch (w) {
+      case 0: merge(std::integral_constant<int, 0>{}); break;
+      case 1: merge(std::integral_constant<int, 1>{}); break;
+      case 2: merge(std::integral_constant<int, 2>{}); break;
+      default: merge(std::integral_constant<int, 3>{}); break;
     }
-    if (w == 0 && (lane & 3) == 0 && rrow < p.rows && sr.ok) {
+    if (w == 0 && grp == 0 && rrow < p.rows && sr.ok) {
       const float l2 = lsum > 0.f ? M + __builtin_amdgcn_logf(lsum) : -INFINITY;
       if (split) p.lse_acc[slot_row] = l2;
       else p.lse[ro] = l2 * kLn2;
