@@ -380,7 +380,8 @@ __device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh
 // current one's epilogue.
 // LDS: per wave two 16-token transfer slots + merge statistics; with the FP8
 // cache the slots hold FP8 images (2 x 10496 B) and a third region holds the
-// dequantised bf16 slice the wave computes on.
+// dequantised bf16 slice the wave computes on.  At a chunk end the waves merge
+// their partial outputs through the slot just consumed.
 template <bool kFp8>
 struct TsLayout {
   static constexpr int kSlot = kFp8 ? kF8SliceBytes : kSliceBytes;
@@ -706,8 +707,11 @@ decode_tokensplit(DecodeParams p) {
 // LDS, so their P blocks share a reference; P goes to LDS and PV is split by
 // output dims (128 per wave, all 64 rows), which reads every V element of the
 // page from LDS once per workgroup.
-// LDS: two page buffers, P [64 rows x 64 tokens] bf16, the per-page row maxima
-// of both token groups, alpha, and the end-of-chunk (m, l) of both token groups.
+// LDS: two page buffers (bf16 pages, or FP8 pages in their first 82 KB), P
+// [64 rows x 64 tokens] bf16, the per-page row maxima of both token groups,
+// alpha, the end-of-chunk (m, l) of both token groups, the token-sparse row
+// offsets and the FP8 page's scale table.  At a chunk end the page buffers
+// stage each wave's output rows.
 constexpr int kPsRows = 64;
 constexpr int kPsPbuf = 2 * kPageBytes;
 constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
