@@ -137,6 +137,31 @@ def test_large_configs_sampled(env, cfg):
     del torch
 
 
+# ------------------------------------------------------------------ maximum sizes
+def test_max_batch(env):
+    """MLA_MAX_BATCH = 8192 sequences (the metadata kernel's on-chip prefix sums
+    at their limit): metadata bit-exact, every output row against the oracle."""
+    w = make_workload(np.random.default_rng(81).integers(0, 131, size=8192), s_q=1, h_q=16, seed=81)
+    md, ns, out, lse = run(env, w)
+    md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
+    assert np.array_equal(md, md_ref) and np.array_equal(ns, ns_ref)
+    check(out, lse, *env[2].decode(w), what="8192 sequences")
+
+
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_one_long_sequence(env, h_q):
+    """One sequence of 2^20 tokens (16384 pages, split across every part), 16
+    rows (token-split kernel) and 64 rows (pair-split kernel)."""
+    w = make_workload([1 << 20], s_q=1, h_q=h_q, seed=82 + h_q)
+    md, ns, out, lse = run(env, w)
+    md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
+    assert np.array_equal(md, md_ref) and np.array_equal(ns, ns_ref)
+    assert ns[-1] == np.count_nonzero(md[:, 0] < w.batch)  # one chunk per non-empty part
+    sel = np.arange(0, h_q, 3)
+    ref_out, ref_lse = env[2].decode(w, sel=sel)
+    check(out, lse, ref_out, ref_lse, sel=sel, what=f"2^20 tokens, {h_q} rows")
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # lens, s_q, h_q, h_kv, causal, num_parts
