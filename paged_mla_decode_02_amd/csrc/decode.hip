@@ -1229,14 +1229,15 @@ decode_pairsplit(DecodeParams p) {
   }
 }
 
-template <typename K>
-hipError_t launch_one(K kernel, int lds, const DecodeParams& p, hipStream_t stream) {
-  // allow the kernel more than the default 64 KB of dynamic LDS (once per process)
+template <auto Kernel>
+hipError_t launch_one(int lds, const DecodeParams& p, hipStream_t stream) {
+  // allow the kernel more than the default 64 KB of dynamic LDS (once per
+  // process and kernel: each kernel is its own instantiation)
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      hipFuncSetAttribute((const void*)Kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int grid = p.num_parts * p.m_tiles * p.h_kv;
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL(Kernel, dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
@@ -1244,12 +1245,12 @@ hipError_t launch_one(K kernel, int lds, const DecodeParams& p, hipStream_t stre
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (tile_rows_for(p.rows) == 16 && !p.sparse) {
-    if (p.kv_fp8) return launch_one(decode_tokensplit<true>, TsLayout<true>::kLds, p, stream);
-    return launch_one(decode_tokensplit<false>, TsLayout<false>::kLds, p, stream);
+    if (p.kv_fp8) return launch_one<decode_tokensplit<true>>(TsLayout<true>::kLds, p, stream);
+    return launch_one<decode_tokensplit<false>>(TsLayout<false>::kLds, p, stream);
   }
-  if (p.kv_fp8) return launch_one(decode_pairsplit<false, true>, kPsLds, p, stream);
-  if (p.sparse) return launch_one(decode_pairsplit<true, false>, kPsLds, p, stream);
-  return launch_one(decode_pairsplit<false, false>, kPsLds, p, stream);
+  if (p.kv_fp8) return launch_one<decode_pairsplit<false, true>>(kPsLds, p, stream);
+  if (p.sparse) return launch_one<decode_pairsplit<true, false>>(kPsLds, p, stream);
+  return launch_one<decode_pairsplit<false, false>>(kPsLds, p, stream);
 }
 
 }  // namespace mla
