@@ -386,8 +386,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(collectives and sharding are out of scope); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(no collectives or sharding); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
