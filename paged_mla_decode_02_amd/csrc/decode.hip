@@ -1133,12 +1133,10 @@ decode_pairsplit(DecodeParams p) {
         };
         PvOps ops[2];
         ops[0] = load_ops(0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           if (ks + 1 < 4) {
             ops[(ks + 1) & 1] = load_ops(ks + 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
           }
           const PvOps& o = ops[ks & 1];
 #pragma unroll
@@ -1146,7 +1144,6 @@ decode_pairsplit(DecodeParams p) {
             O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
             O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
           if (has_next) {
             for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
                  ++i)
