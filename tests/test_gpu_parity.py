@@ -195,6 +195,35 @@ def test_edge_cases(env, lens, s_q, h_q, h_kv, causal, P):
     check(out, lse, *ref, what=f"edge {lens} s_q={s_q} h_q={h_q} h_kv={h_kv} P={P}")
 
 
+# ------------------------------------------------------------ random shapes
+def random_shape(seed):
+    """A seeded draw of batch, lengths (with 0, 1 and page-edge lengths mixed
+    in), s_q, heads, causal mask and part count."""
+    g = np.random.Generator(np.random.PCG64(1000 + seed))
+    batch = int(g.integers(1, 13))
+    pool = [0, 1, 63, 64, 65, 127, 128, 129]
+    lens = [int(g.choice(pool)) if g.random() < 0.3 else int(g.integers(1, 3000)) for _ in range(batch)]
+    s_q = int(g.integers(1, 5))
+    h_kv = int(g.choice([1, 1, 2]))
+    h_q = h_kv * int(g.choice([1, 4, 8, 16, 17, 32, 64]))
+    causal = bool(g.random() < 0.5)
+    P = None if g.random() < 0.5 else int(g.integers(1, 40))
+    return lens, s_q, h_q, h_kv, causal, P
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes(env, seed):
+    lens, s_q, h_q, h_kv, causal, P = random_shape(seed)
+    w = make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal, seed=seed,
+                      extra_pages=1, poison_tail=True, outliers=bool(seed % 2))
+    md, ns, out, lse = run(env, w, num_parts=P)
+    md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
+    assert np.array_equal(md, md_ref) and np.array_equal(ns, ns_ref)
+    ref = env[2].decode(w)
+    check(out, lse, *ref, what=f"random seed={seed}: lens={lens} s_q={s_q} h_q={h_q} h_kv={h_kv} "
+                               f"causal={causal} P={P}")
+
+
 def test_large_scores_rescale(env):
     """Scores far apart (|x| up to ~300 in log2 units) force the lazy rescale path."""
     w = make_workload([3000, 640, 129], s_q=2, h_q=64, causal=True, seed=21)
