@@ -184,3 +184,28 @@ def test_append_fp8_then_decode(env):
     ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(ref8), cache_seqlens=lens2))
     o = out.float().cpu().numpy().astype(np.float64).reshape(-1, 512)
     check(o, lse.cpu().numpy().astype(np.float64).reshape(-1), ro, rl, "append fp8 -> decode")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_fp8_random_shapes(env, seed):
+    """Seeded draws of batch, lengths (0, 1 and page edges mixed in), s_q, heads,
+    causal mask and part count over FP8 caches with NaN codes past every end."""
+    _, _, orc, fp8, _, _ = env
+    g = np.random.Generator(np.random.PCG64(2000 + seed))
+    batch = int(g.integers(1, 9))
+    pool = [0, 1, 63, 64, 65, 128, 129]
+    lens = [int(g.choice(pool)) if g.random() < 0.3 else int(g.integers(1, 2500)) for _ in range(batch)]
+    s_q = int(g.integers(1, 4))
+    h_kv = int(g.choice([1, 1, 2]))
+    h_q = h_kv * int(g.choice([1, 8, 16, 24, 64]))
+    causal = bool(g.random() < 0.5)
+    parts = None if g.random() < 0.5 else int(g.integers(1, 30))
+    w = make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, causal=causal, seed=3000 + seed)
+    kc8 = poison_tails(w, workloads.make_fp8_cache(w, seed=seed))
+    go, gl = decode_fp8(env, w, kc8, num_parts=parts)
+    clean = kc8.copy()
+    lat = clean[..., :512]
+    lat[lat == 0x7F] = 0
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(clean)))
+    check(go, gl, ro, rl, f"fp8 random seed={seed}: lens={lens} s_q={s_q} h_q={h_q} h_kv={h_kv} "
+                          f"causal={causal} parts={parts}")
