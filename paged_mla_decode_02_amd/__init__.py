@@ -418,6 +418,10 @@ def mla_sparse_prepare(indices: torch.Tensor, indptr: torch.Tensor, s_q: int, bl
     _require(counts, "counts", torch.int32)
     if offsets.shape[0] < indices.shape[0] + 64:
         raise ValueError("offsets needs nnz + 64 entries")
+    if indices.numel() == 0:
+        # no row lists anything: the kernel reads no entry, but the C ABI takes
+        # no null pointer (an empty tensor has none)
+        indices = torch.zeros(1, dtype=torch.int32, device=dev)
     _check(_lib.mla_sparse_prepare(indices.data_ptr(), indptr.data_ptr(), b, s_q, block_table.data_ptr(),
                                    block_table.shape[1], cache_seqlens.data_ptr(), num_pages, h_kv,
                                    offsets.data_ptr(), counts.data_ptr(), _stream(dev)))

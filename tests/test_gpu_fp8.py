@@ -65,8 +65,9 @@ def check(go, gl, ro, rl, what):
     ninf = np.isneginf(rl)
     assert np.all(np.isfinite(go)), what
     assert np.array_equal(np.isneginf(gl), ninf), what
-    rel = np.linalg.norm(go - ro) / np.linalg.norm(ro)
-    err = np.max(np.abs(gl[~ninf] - rl[~ninf]))
+    nr = np.linalg.norm(ro)
+    rel = np.linalg.norm(go - ro) / nr if nr > 0 else np.linalg.norm(go)  # all rows empty: exact zeros
+    err = np.max(np.abs(gl[~ninf] - rl[~ninf])) if np.any(~ninf) else 0.0
     assert rel <= OUT_TOL and err <= LSE_TOL, f"{what}: rel {rel:.2e} lse {err:.2e}"
 
 

@@ -38,7 +38,8 @@ def check(go, gl, ro, rl, what):
     assert np.all(np.isfinite(go)), what
     assert np.array_equal(np.isneginf(gl), ninf), what
     assert np.all(go[ninf] == 0), what
-    rel = np.linalg.norm(go - ro) / np.linalg.norm(ro)
+    nr = np.linalg.norm(ro)
+    rel = np.linalg.norm(go - ro) / nr if nr > 0 else np.linalg.norm(go)  # all rows empty: exact zeros
     err = np.max(np.abs(gl[~ninf] - rl[~ninf])) if np.any(~ninf) else 0.0
     assert rel <= OUT_TOL and err <= LSE_TOL, f"{what}: rel {rel:.2e} lse {err:.2e}"
 
@@ -95,3 +96,30 @@ def test_sparse_decode_large_sampled(env):
     go = out.float().cpu().numpy().astype(np.float64).reshape(-1, 512)[sel]
     gl = lse.cpu().numpy().astype(np.float64).reshape(-1)[sel]
     check(go, gl, ro, rl, "large sparse")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sparse_decode_random_shapes(env, seed):
+    """Seeded draws of lengths, s_q, heads, top-k, invalid entries, shuffled and
+    empty rows, and part count."""
+    torch, mla, sparse, dev = env
+    g = np.random.Generator(np.random.PCG64(4000 + seed))
+    batch = int(g.integers(1, 7))
+    lens = [int(g.choice([0, 1, 64, 65])) if g.random() < 0.25 else int(g.integers(1, 3000)) for _ in range(batch)]
+    s_q = int(g.integers(1, 4))
+    h_kv = int(g.choice([1, 1, 2]))
+    h_q = h_kv * int(g.choice([8, 16, 64, 128]))
+    topk = int(g.integers(1, 1500))
+    invalid = float(g.choice([0.0, 0.2]))
+    empty = tuple(int(v) for v in g.choice(batch * s_q, size=int(g.integers(0, 2)), replace=False))
+    parts = None if g.random() < 0.5 else int(g.integers(1, 24))
+    w = make_workload(lens, s_q=s_q, h_q=h_q, h_kv=h_kv, seed=5000 + seed)
+    idx, ptr = make_sparse_indices(w, topk, seed=seed, invalid=invalid, shuffle=bool(seed % 2), empty_rows=empty)
+    q, kc, bt, sl, ti, tp = upload(torch, w, idx, ptr, dev)
+    out, lse = mla.flash_mla_sparse_with_kvcache(q, kc, bt, sl, ti, tp, softmax_scale=w.scale, num_parts=parts)
+    torch.cuda.synchronize()
+    ro, rl = sparse.decode(w, idx, ptr)
+    go = out.float().cpu().numpy().astype(np.float64).reshape(-1, 512)
+    gl = lse.cpu().numpy().astype(np.float64).reshape(-1)
+    check(go, gl, ro, rl, f"sparse random seed={seed}: lens={lens} s_q={s_q} h_q={h_q} h_kv={h_kv} "
+                          f"topk={topk} invalid={invalid} empty={empty} parts={parts}")
