@@ -276,7 +276,8 @@ int mla_decode_splitkv_fp8(const void* q, const void* kcache_fp8, int64_t num_pa
  * mla_sparse_prepare: keeps the valid entries of every row, in order, as the
  *   byte offsets of their cache rows (KV head 0): offsets[indptr[v] + i] for
  *   i < counts[v].
- *   indices  int32 [indptr[batch*s_q]] device
+ *   indices  int32 [indptr[batch*s_q]] device; never NULL, also when every list
+ *            is empty (then no entry is read: any valid device address does)
  *   indptr   int32 [batch*s_q + 1] device, non-decreasing, indptr[0] = 0
  *   block_table, cache_seqlens, num_pages, max_blocks, h_kv: as for the decode
  *   offsets  uint32 [indptr[batch*s_q] + 64] device, out (the 64 spare entries
