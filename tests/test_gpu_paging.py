@@ -105,3 +105,26 @@ def test_append_empty_batch(env):
     out = mla.mla_kv_append(torch.empty((0, 1, 1, 576), dtype=torch.bfloat16, device=dev), e,
                             torch.empty((0, 4), dtype=torch.int32, device=dev), kc)
     assert out.shape == (0,)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_append_random_shapes(env, seed):
+    """Seeded draws of batch, lengths (page edges mixed in), tokens per append and
+    KV heads; the whole cache after the append is compared byte for byte."""
+    torch, mla, _, paging, dev = env
+    g = np.random.Generator(np.random.PCG64(6000 + seed))
+    batch = int(g.integers(1, 12))
+    lens = [int(g.choice([0, 1, 63, 64, 127, 128])) if g.random() < 0.4 else int(g.integers(0, 700))
+            for _ in range(batch)]
+    s_new = int(g.choice([1, 1, 2, 5, 64, 65]))
+    h_kv = int(g.choice([1, 2]))
+    w, before, new_kv = make_append_case(lens, s_new, h_kv=h_kv, h_q=2 * h_kv, seed=7000 + seed, extra_pages=1)
+    kc = dev16(torch, w.kcache, dev).view(torch.bfloat16)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(before).to(dev)
+    new_lens = mla.mla_kv_append(dev16(torch, new_kv, dev).view(torch.bfloat16), sl, bt, kc)
+    torch.cuda.synchronize()
+    ref, ref_lens = paging.kv_append(w.kcache, w.block_table, before, new_kv)
+    what = f"append random seed={seed}: lens={lens} s_new={s_new} h_kv={h_kv}"
+    assert np.array_equal(kc.view(torch.int16).cpu().numpy().view(np.uint16), ref), what
+    assert np.array_equal(new_lens.cpu().numpy(), ref_lens), what
