@@ -178,3 +178,60 @@ def test_decode_rejects_scale(lib, scale):
             FAKE, FAKE, FAKE, 1 << 30, None]
     assert lib.mla_decode_paged(*args) == MLA_ERR_INVALID
     assert b"softmax_scale" in lib.mla_last_error()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), MLA_ERR_INVALID),
+    (dict(s_q=0), MLA_ERR_INVALID),
+    (dict(d_qk=512), MLA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=100), MLA_ERR_WORKSPACE),
+    (dict(batch=9000), MLA_ERR_UNSUPPORTED),
+])
+def test_decode_fp8_rejects(lib, over, code):
+    lib.mla_decode_paged_fp8.argtypes = lib.mla_decode_paged.argtypes
+    assert lib.mla_decode_paged_fp8(*decode_args(**over)) == code
+    assert lib.mla_last_error()
+
+
+def sparse_prepare_args(**over):
+    a = dict(indices=FAKE, indptr=FAKE, batch=2, s_q=1, bt=FAKE, max_blocks=4, seqlens=FAKE, num_pages=10,
+             h_kv=1, offsets=FAKE, counts=FAKE, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=-1), MLA_ERR_INVALID),
+    (dict(s_q=0), MLA_ERR_INVALID),
+    (dict(indices=None), MLA_ERR_INVALID),  # also when every list is empty
+    (dict(counts=None), MLA_ERR_INVALID),
+    (dict(num_pages=60000), MLA_ERR_UNSUPPORTED),  # 4.4 GB: beyond 32-bit row offsets
+    (dict(batch=0), MLA_OK),  # nothing to do, no HIP call
+])
+def test_sparse_prepare_rejects(lib, over, code):
+    P, I = ctypes.c_void_p, ctypes.c_int
+    lib.mla_sparse_prepare.argtypes = [P, P, I, I, P, I, P, ctypes.c_int64, I, P, P, P]
+    assert lib.mla_sparse_prepare(*sparse_prepare_args(**over)) == code
+
+
+def sparse_decode_args(**over):
+    a = dict(q=FAKE, kcache=FAKE, num_pages=10, offsets=FAKE, indptr=FAKE, counts=FAKE, batch=2, s_q=1,
+             h_q=16, h_kv=1, d_qk=576, dv=512, page=64, md=FAKE, num_parts=8, ns=FAKE, scale=0.07,
+             out=FAKE, lse=FAKE, ws=FAKE, ws_bytes=(2 + 8) * 16 * 513 * 4, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(batch=0), MLA_ERR_INVALID),
+    (dict(batch=4097, s_q=2), MLA_ERR_UNSUPPORTED),  # batch * s_q query rows above MLA_MAX_BATCH
+    (dict(d_qk=512), MLA_ERR_UNSUPPORTED),
+    (dict(ws_bytes=100), MLA_ERR_WORKSPACE),
+    (dict(num_pages=60000), MLA_ERR_UNSUPPORTED),
+])
+def test_sparse_decode_rejects(lib, over, code):
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.mla_sparse_decode.argtypes = [P, P, ctypes.c_int64, P, P, P, I, I, I, I, I, I, I, P, I, P,
+                                      ctypes.c_float, P, P, P, SZ, P]
+    assert lib.mla_sparse_decode(*sparse_decode_args(**over)) == code
+    assert lib.mla_last_error()
