@@ -11,17 +11,24 @@ reported beside the step (schedule_ms, ms_per_step_with_schedule).  The timed
 steps are captured, in order, into HIP graphs of up to 25 consecutive steps each
 and every graph is replayed once (a graph launch costs the GPU ~5 us, which one
 graph per step would add to every step).  Step i reads cache copy i mod C, with
-enough copies C that the working set exceeds the 256 MB MALL, so reads come
-from HBM.
+enough copies C that the working set exceeds twice the 256 MB MALL, so reads
+come from HBM.
 
-Prints ONE JSON line:
+The headline workload (--config, default spec_decode_causal, the largest) gives
+the line's value; every other workload is timed in the same run and listed under
+"workloads" with the same fields.  Prints ONE JSON line:
   value          algorithmic bytes per step / wall time per step (TB/s)
-  roofline       the decode kernel's achieved bandwidth (or MFMA rate) against
-                 MI355X's published peak, from HIP events around graphs of
-                 back-to-back launches of the kernel
-  cpu_baseline   the fp64 CPU oracle on the host cores (a reported baseline)
+  tflops         algorithmic flops per step / wall time per step
+  roofline       the decode kernel against MI355X's published peak (HBM or
+                 bf16 MFMA, whichever bounds the workload), from HIP events
+                 around graphs of back-to-back launches of the kernel
+  step_percentiles_ms  p10 / median / p90 of >= 100 eager steps
+  copy_bandwidth a plain device copy's rate on this GPU (context)
+  cpu_baseline   the fp64 CPU oracle on the host cores over a bounded sample
+                 of the headline workload (a reported baseline)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {0..4}]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config {0..4}] [--only]
+                       [--kv {bf16,fp8}] [--op {decode,absorb,append,sparse}]
 """
 from __future__ import annotations
 
@@ -94,26 +101,61 @@ def traffic_from_profiles(workload, launch_kind):
     return None
 
 
-def cpu_baseline(w, bytes_step, target_s):
-    """The oracle as it stands, on the host cores, over the whole workload
-    repeated until about target_s seconds of CPU work have run."""
+def cpu_baseline(w, target_s, row_bytes=576 * 2):
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    workload: whole passes repeated for about target_s seconds when a pass is
+    shorter than that, else the first n sequences (all their query rows) with n
+    chosen from a one-sequence probe so that the run takes about target_s."""
+    import numpy as np
+
     import oracle
     orc = oracle.default()
     cores = len(os.sched_getaffinity(0))
     orc.set_threads(cores)
-    runs = 0
+    per_seq = w.s_q * w.h_q
+
+    def sample_bytes_flops(n):
+        sub = workloads_subset(w, n)
+        by, fl, _ = algorithmic(sub, row_bytes)
+        return by, fl
+
     t0 = time.perf_counter()
-    while True:
-        orc.decode(w)
-        runs += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or runs >= 1000:
-            break
-    per_run = el / runs
-    return {"value": round(bytes_step / per_run / 1e12, 6), "unit": "TB/s",
-            "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"the whole workload ({w.batch} sequences, {w.batch * w.s_q * w.h_q} query rows), "
-                      f"fp64, repeated {runs}x over {el:.1f} s; {per_run * 1e3:.1f} ms per pass"}
+    orc.decode(w, sel=np.arange(per_seq, dtype=np.int64))
+    probe = max(time.perf_counter() - t0, 1e-6)
+    if probe * w.batch <= target_s:
+        runs = 0
+        t0 = time.perf_counter()
+        while True:
+            orc.decode(w)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or runs >= 1000:
+                break
+        n, per_run = w.batch, el / runs
+        what = f"the whole workload ({w.batch} sequences, {w.batch * per_seq} query rows), fp64, " \
+               f"repeated {runs}x over {el:.1f} s; {per_run * 1e3:.1f} ms per pass"
+    else:
+        n = int(min(w.batch, max(1, target_s / probe)))
+        for _ in range(2):  # a second, larger sample when the probe overestimated
+            t0 = time.perf_counter()
+            orc.decode(w, sel=np.arange(n * per_seq, dtype=np.int64))
+            per_run = time.perf_counter() - t0
+            if per_run >= 0.5 * target_s or n >= w.batch:
+                break
+            n = int(min(w.batch, n * target_s / per_run))
+        what = f"the first {n} of {w.batch} sequences ({n * per_seq} query rows, " \
+               f"{int(w.cache_seqlens[:n].sum())} cached tokens), fp64, one pass of {per_run:.1f} s"
+    by, fl = sample_bytes_flops(n)
+    return {"value": round(by / per_run / 1e12, 6), "unit": "TB/s", "cores": orc.num_threads(), "kind": "oracle",
+            "tflops": round(fl / per_run / 1e12, 6), "sample": what}
+
+
+def workloads_subset(w, n):
+    """The first n sequences of workload w (same cache and tables), for sizing
+    the CPU baseline's sample."""
+    import dataclasses
+    return dataclasses.replace(w, batch=n, cache_seqlens=w.cache_seqlens[:n], block_table=w.block_table[:n],
+                               q=w.q[:n])
 
 
 def timed_steps(torch, step, K, W, eager=False):
@@ -326,7 +368,7 @@ def bench_sparse(args, torch, mla, workloads, dev):
     fl = 2 * kept * w.h_q * (576 + 512)
 
     def step(c):
-        mla.mla_sparse_decode(q, kcs[c], offs, tp, counts, 512, md, ns, w.scale, out, lse, ws)
+        mla.mla_sparse_decode(q, kcs[c], offs, tp, counts, 512, md, ns, w.scale, out, lse, ws, nnz=ti.shape[0])
 
     for c in range(min(3, ncopies)):
         step(c)
@@ -368,8 +410,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (default: memory-bound)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--config", type=int, default=3,
+                    help="headline workload index 0..4 (default 3: spec_decode_causal, the largest)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline workload only (by default every workload is timed and listed "
+                         "under 'workloads')")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of graphs")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
@@ -420,19 +466,120 @@ def main():
     if args.op == "sparse":
         bench_sparse(args, torch, mla, workloads, dev)
         return
-    cfg = workloads.CONFIGS[args.config]
-    w = workloads.config_workload(args.config)
     fp8 = args.kv == "fp8"
-    bytes_step, flops_step, kv_bytes = algorithmic(w, mla.FP8_ROW_BYTES if fp8 else 576 * 2)
+    K, W = args.steps, args.warmup
+    headline = measure_decode(args.config, K, W, torch, mla, workloads, dev, fp8, eager=args.eager)
+    others = []
+    if not args.only:
+        for idx in sorted(workloads.CONFIGS):
+            if idx != args.config:
+                others.append(measure_decode(idx, max(K, 100), W, torch, mla, workloads, dev, fp8))
+                torch.cuda.empty_cache()
+    copy = copy_bandwidth(torch, dev)
 
-    # inputs resident in HBM; enough cache copies to defeat the MALL
+    h = headline
+    line = {
+        "metric": ("paged MLA decode, FP8 latent cache (bf16 compute): achieved TB/s & TFLOPS, % of MI355X "
+                   "roofline") if fp8 else "paged MLA decode bf16: achieved TB/s & TFLOPS, % of MI355X roofline",
+        "value": h["step_tbps"],
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": h["step_ms"],
+        "schedule_ms": h["kernel_ms"]["metadata"],
+        "ms_per_step_with_schedule": round(h["step_ms"] + h["kernel_ms"]["metadata"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": h["config"],
+        "tflops": h["step_tflops"],
+        "roofline_frac_step": h["roofline_frac_step"],
+        "algorithmic": h["algorithmic"],
+        "kernel_ms": h["kernel_ms"],
+        "step_percentiles_ms": h["step_percentiles_ms"],
+        "roofline": h["roofline"],
+        "copy_bandwidth": copy,
+        "workloads": [summary(h)] + [summary(o) for o in others],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(h["workload"], args.cpu_seconds,
+                                            mla.FP8_ROW_BYTES if fp8 else 576 * 2)
+    print(json.dumps(line))
+
+
+def summary(r):
+    """The per-workload entry of the JSON line (everything but the inputs)."""
+    keys = ("config", "step_ms", "step_tbps", "step_tflops", "roofline_frac_step", "kernel_ms",
+            "step_percentiles_ms", "roofline", "decode_hbm_frac", "decode_mfma_frac")
+    out = {k: r[k] for k in keys}
+    out["workload"] = r["config"]["workload"]
+    return out
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=20):
+    """A plain device-to-device copy of nbytes (torch copy_), events around reps
+    back-to-back copies: the streaming rate the chip reaches on this machine, as
+    context for the kernels' HBM fractions (read + write bytes per second)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": round(ms, 4), "GBs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "kind": "torch copy_ (device to device)"}
+
+
+def eager_percentiles(torch, fn, n):
+    """p10 / median / p90 (ms) of n eager launches of fn(i), each bracketed by
+    HIP events on the launch stream; a GPU spin first lets the host enqueue all
+    of them, so the launches run back to back (each bracket includes the
+    dispatch of its first kernel)."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(60e6))
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    d = np.array([s.elapsed_time(e) for s, e in ev])
+    return {"p10": round(float(np.percentile(d, 10)), 5), "median": round(float(np.median(d)), 5),
+            "p90": round(float(np.percentile(d, 90)), 5), "launches": n,
+            "timing": "HIP events around each eager step (decode + combine), queue pre-filled"}
+
+
+def measure_decode(idx, K, W, torch, mla, workloads, dev, fp8, eager=False):
+    """Time one workload's decode step (decode + combine) and its kernels."""
+    import numpy as np
+    cfg = workloads.CONFIGS[idx]
+    w = workloads.config_workload(idx)
+    row_bytes = mla.FP8_ROW_BYTES if fp8 else 576 * 2
+    bytes_step, flops_step, kv_bytes = algorithmic(w, row_bytes)
+
+    # inputs resident in HBM; enough cache copies that the rotation exceeds twice
+    # the MALL (at most 32 copies: the tiny workload stays cache-resident)
     if fp8:
-        kc_host = torch.from_numpy(workloads.make_fp8_cache(w, seed=args.config))
+        kc_host = torch.from_numpy(workloads.make_fp8_cache(w, seed=idx))
     else:
         kc_host = torch.from_numpy(w.kcache.view(np.int16))
     kc_bytes = kc_host.numel() * kc_host.element_size()
-    ncopies = max(1, math.ceil(2 * MALL_BYTES / kc_bytes))
+    ncopies = min(32, max(1, math.ceil(2 * MALL_BYTES / kc_bytes)))
+    mall_defeated = ncopies * kc_bytes >= 2 * MALL_BYTES
     kcs = [kc_host.to(dev) if fp8 else kc_host.to(dev).view(torch.bfloat16) for _ in range(ncopies)]
+    del kc_host
     decode_fn = mla.mla_decode_splitkv_fp8 if fp8 else mla.mla_decode_splitkv
     q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
     bt = torch.from_numpy(w.block_table).to(dev)
@@ -447,58 +594,43 @@ def main():
     def schedule():
         mla.mla_get_metadata(sl, w.rows, w.h_kv, num_parts=P, out=(md, ns))
 
-    def step(c, evs=None):
-        if evs is not None:
-            evs[0].record()
+    def decode_one(c):
         decode_fn(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
-        if evs is not None:
-            evs[1].record()
-        mla.mla_combine_splits(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
-        if evs is not None:
-            evs[2].record()
 
-    K, W = args.steps, args.warmup
+    def combine_one(c):
+        mla.mla_combine_splits(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
+
+    def step(c):
+        decode_one(c)
+        combine_one(c)
+
     schedule()
     for i in range(3):
         step(i % ncopies)  # eager warm-up (kernel attributes, allocator)
     torch.cuda.synchronize()
+    # the rows of split sequences get out / lse from the combine, the others from the decode
+    chunks = np.diff(ns.cpu().numpy().astype(np.int64))
+    per_seq_out = w.s_q * w.h_q * (512 * 2 + 4)
+    combine_out_bytes = int(np.count_nonzero(chunks > 1)) * per_seq_out
+    decode_bytes = bytes_step - combine_out_bytes
 
     # timed region: exactly K steps of decode + combine, replayed from graphs
-    ms_per_step, mode, per_graph = timed_steps(torch, lambda i: step(i % ncopies), K, W, eager=args.eager)
-
-    # per-kernel durations: HIP events around graphs of 25 back-to-back launches of
-    # one kernel (graph_kernel_ms); without graphs, events around every launch
-    combine_fn = lambda c: mla.mla_combine_splits(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
-    decode_one = lambda c: decode_fn(q, kcs[c], bt, sl, w.dv, md, ns, w.causal, w.scale, out, lse, ws)
+    ms_per_step, mode, per_graph = timed_steps(torch, lambda i: step(i % ncopies), K, W, eager=eager)
     if mode == "hip_graph":
         (dec_ms, dec_g), (comb_ms, _), (meta_ms, _) = graph_kernel_ms(
-            torch, [lambda i: decode_one(i % ncopies), lambda i: combine_fn(i % ncopies), lambda i: schedule()])
-        n_ev, timing = 100, "HIP events around graph replays of 25 back-to-back launches of the kernel, 4 graphs"
+            torch, [lambda i: decode_one(i % ncopies), lambda i: combine_one(i % ncopies), lambda i: schedule()])
+        timing = "HIP events around graph replays of 25 back-to-back launches of the kernel, 4 graphs"
     else:
-        n_ev = min(K, 100)
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(40e6))
-        for i in range(n_ev):
-            step(i % ncopies, events[i])
-        torch.cuda.synchronize()
-        durs = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(2)] for i in range(n_ev)])
-        dec_ms, comb_ms = (float(x) for x in durs.mean(axis=0))
         dec_g = None
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
-        torch.cuda._sleep(int(20e6))
-        for i in range(n_ev):
-            sev[i][0].record()
-            schedule()
-            sev[i][1].record()
-        torch.cuda.synchronize()
-        meta_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
-        timing = "HIP events around every eager launch"
+        dec_ms = eager_percentiles(torch, lambda i: decode_one(i % ncopies), 100)["median"]
+        comb_ms = eager_percentiles(torch, lambda i: combine_one(i % ncopies), 100)["median"]
+        meta_ms = eager_percentiles(torch, lambda i: schedule(), 100)["median"]
+        timing = "median of HIP events around 100 eager launches of the kernel"
+    pct = eager_percentiles(torch, lambda i: step(i % ncopies), max(100, K))
 
-    tbps = bytes_step / (ms_per_step * 1e-3) / 1e12
     intensity = flops_step / bytes_step
     bound = "hbm" if intensity < RIDGE else "mfma"
-    dec_gbs = bytes_step / (dec_ms * 1e-3) / 1e9
+    dec_gbs = decode_bytes / (dec_ms * 1e-3) / 1e9
     dec_tflops = flops_step / (dec_ms * 1e-3) / 1e12
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -506,49 +638,39 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(dec_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)}
-    traffic = traffic_from_profiles(cfg["name"], "decode_fp8" if fp8 else "decode")
-    roof["traffic"] = traffic
+    roof["traffic"] = traffic_from_profiles(cfg["name"], "decode_fp8" if fp8 else "decode")
     roof["kernel"] = "decode (mla_decode_splitkv_fp8)" if fp8 else "decode (mla_decode_splitkv)"
     roof["launch_ms"] = round(float(dec_ms), 5)
+    roof["algorithmic_per_launch"] = ({"bytes": int(decode_bytes)} if bound == "hbm" else {"flops": int(flops_step)})
 
-    line = {
-        "metric": ("paged MLA decode, FP8 latent cache (bf16 compute): achieved TB/s & TFLOPS, % of MI355X "
-                   "roofline") if fp8 else "paged MLA decode bf16: achieved TB/s & TFLOPS, % of MI355X roofline",
-        "value": round(tbps, 4),
-        "unit": "TB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 5),
-        "schedule_ms": round(meta_ms, 5),
-        "ms_per_step_with_schedule": round(ms_per_step + meta_ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    res = {
+        "workload": w,
         "config": {
             "workload": cfg["name"], "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "h_kv": w.h_kv,
             "d_qk": 576, "dv": 512, "page_block_size": 64, "causal": w.causal,
             "seqlens": {"kind": cfg["lens"][0], "params": list(cfg["lens"][1:]), "seed": w.seed,
                         "total_tokens": int(w.cache_seqlens.sum())},
-            "softmax_scale": w.scale, "num_parts": P, "cache_copies": ncopies, "launch": mode,
-            "steps_per_graph": per_graph,
+            "softmax_scale": w.scale, "num_parts": P, "cache_copies": ncopies, "mall_defeated": mall_defeated,
+            "launch": mode, "steps_per_graph": per_graph,
             "kv_format": "fp8_e4m3 rows of 656 B (4 power-of-two scales, bf16 rope)" if fp8 else "bf16",
         },
-        "tflops": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3),
+        "step_ms": round(ms_per_step, 5),
+        "step_tbps": round(bytes_step / (ms_per_step * 1e-3) / 1e12, 4),
+        "step_tflops": round(flops_step / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline_frac_step": round(max(bytes_step / (HBM_PEAK_GBS * 1e9), flops_step / (BF16_PEAK_TFLOPS * 1e12))
                                     / (ms_per_step * 1e-3), 4),
+        "decode_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4),
         "algorithmic": {"bytes_per_step": int(bytes_step), "flops_per_step": int(flops_step),
-                        "flop_per_byte": round(intensity, 2)},
+                        "flop_per_byte": round(intensity, 2), "decode_bytes": int(decode_bytes),
+                        "combine_out_bytes": int(combine_out_bytes)},
         "kernel_ms": {"metadata": round(float(meta_ms), 5), "decode": round(float(dec_ms), 5),
-                      "combine": round(float(comb_ms), 5),
-                      "decode_per_graph": dec_g, "launches": n_ev, "timing": timing},
+                      "combine": round(float(comb_ms), 5), "decode_per_graph": dec_g, "timing": timing},
+        "step_percentiles_ms": pct,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, bytes_step, args.cpu_seconds)
-    print(json.dumps(line))
+    del kcs, q, bt, sl, md, ns, ws, out, lse
+    return res
 
 
 if __name__ == "__main__":

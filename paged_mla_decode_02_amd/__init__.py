@@ -121,13 +121,30 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _require(t: torch.Tensor, name: str, dtype: torch.dtype) -> None:
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, on_device: bool = True) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if on_device and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    """The kernels index these tensors by batch, row and part: any other shape
+    would send them outside the buffer, so it is refused on the host."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _same_device(dev: torch.device, **tensors) -> None:
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, q on {dev}")
 
 
 def mla_tile_rows(rows_per_kv: int) -> int:
@@ -174,12 +191,13 @@ def mla_get_metadata(cache_seqlens: torch.Tensor, rows_per_kv: int, h_kv: int,
 
 def _decode_call(fn, q, kcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,
                  softmax_scale, out, lse, workspace, fp8=False):
-    _require(q, "q", torch.bfloat16)
-    _require(kcache, "kcache", torch.uint8 if fp8 else torch.bfloat16)
-    _require(block_table, "block_table", torch.int32)
-    _require(cache_seqlens, "cache_seqlens", torch.int32)
-    _require(tile_metadata, "tile_metadata", torch.int32)
-    _require(num_splits, "num_splits", torch.int32)
+    # dtypes and shapes first (host metadata only), then devices
+    _require(q, "q", torch.bfloat16, on_device=False)
+    _require(kcache, "kcache", torch.uint8 if fp8 else torch.bfloat16, on_device=False)
+    _require(block_table, "block_table", torch.int32, on_device=False)
+    _require(cache_seqlens, "cache_seqlens", torch.int32, on_device=False)
+    _require(tile_metadata, "tile_metadata", torch.int32, on_device=False)
+    _require(num_splits, "num_splits", torch.int32, on_device=False)
     if q.dim() != 4 or kcache.dim() != 4 or block_table.dim() != 2:
         raise ValueError("q must be [b, s_q, h_q, d], kcache [pages, 64, h_kv, d], block_table [b, n]")
     b, s_q, h_q, d_qk = q.shape
@@ -188,17 +206,36 @@ def _decode_call(fn, q, kcache, block_table, cache_seqlens, dv, tile_metadata, n
         raise ValueError("kcache rows must be the head dim of q (bf16) or FP8_ROW_BYTES bytes (fp8)")
     if h_kv <= 0 or h_q % h_kv:
         raise ValueError("h_q must be a multiple of h_kv")
+    if block_table.shape[0] != b:
+        raise ValueError(f"block_table must have one row per sequence ({b}), got {block_table.shape[0]}")
+    _shape(cache_seqlens, "cache_seqlens", (b,))
+    _shape(num_splits, "num_splits", (b + 1,))
+    if tile_metadata.dim() != 2 or tile_metadata.shape[1] != 8 or tile_metadata.shape[0] < 1:
+        raise ValueError(f"tile_metadata must be [num_parts, 8], got {tuple(tile_metadata.shape)}")
     num_parts = tile_metadata.shape[0]
     rows = s_q * h_q // h_kv
     dev = q.device
+    if out is not None:
+        _require(out, "out", torch.bfloat16, on_device=False)
+        _shape(out, "out", (b, s_q, h_q, dv))
+    if lse is not None:
+        _require(lse, "lse", torch.float32, on_device=False)
+        _shape(lse, "lse", (b, s_q, h_q))
+    need = (b + num_parts) * h_kv * rows * (dv + 1) * 4
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor")
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace must hold {need} bytes, got {workspace.numel() * workspace.element_size()}")
+    _same_device(dev, q=q, kcache=kcache, block_table=block_table, cache_seqlens=cache_seqlens,
+                 tile_metadata=tile_metadata, num_splits=num_splits)
     if out is None:
         out = torch.empty((b, s_q, h_q, dv), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
-    _require(out, "out", torch.bfloat16)
-    _require(lse, "lse", torch.float32)
     if workspace is None:
-        workspace = torch.empty((b + num_parts) * h_kv * rows * (dv + 1) * 4, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _same_device(dev, out=out, lse=lse, workspace=workspace)
     _check(fn(q.data_ptr(), kcache.data_ptr(), num_pages, block_table.data_ptr(), block_table.shape[1],
               cache_seqlens.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
               num_parts, num_splits.data_ptr(), int(bool(causal)), float(softmax_scale),
@@ -404,20 +441,29 @@ def mla_sparse_prepare(indices: torch.Tensor, indptr: torch.Tensor, s_q: int, bl
     returns (offsets uint32-as-int32 [nnz + 64], counts int32 [batch*s_q])."""
     for t, n in ((indices, "indices"), (indptr, "indptr"), (block_table, "block_table"),
                  (cache_seqlens, "cache_seqlens")):
-        _require(t, n, torch.int32)
+        _require(t, n, torch.int32, on_device=False)
+    if cache_seqlens.dim() != 1 or indices.dim() != 1 or indptr.dim() != 1 or block_table.dim() != 2:
+        raise ValueError("cache_seqlens, indices and indptr must be 1-D and block_table [batch, max_blocks]")
     b = cache_seqlens.shape[0]
     rows = indptr.shape[0] - 1
     if rows != b * s_q:
         raise ValueError("indptr must have batch * s_q + 1 entries")
+    if block_table.shape[0] != b:
+        raise ValueError(f"block_table must have one row per sequence ({b}), got {block_table.shape[0]}")
+    if offsets is not None:
+        _require(offsets, "offsets", torch.int32, on_device=False)
+        if offsets.dim() != 1 or offsets.shape[0] < indices.shape[0] + 64:
+            raise ValueError("offsets needs nnz + 64 entries")
+    if counts is not None:
+        _require(counts, "counts", torch.int32, on_device=False)
+        _shape(counts, "counts", (rows,))
     dev = indices.device
+    _same_device(dev, indices=indices, indptr=indptr, block_table=block_table, cache_seqlens=cache_seqlens)
     if offsets is None:
         offsets = torch.empty(indices.shape[0] + 64, dtype=torch.int32, device=dev)
     if counts is None:
         counts = torch.empty(rows, dtype=torch.int32, device=dev)
-    _require(offsets, "offsets", torch.int32)
-    _require(counts, "counts", torch.int32)
-    if offsets.shape[0] < indices.shape[0] + 64:
-        raise ValueError("offsets needs nnz + 64 entries")
+    _same_device(dev, offsets=offsets, counts=counts)
     if indices.numel() == 0:
         # no row lists anything: the kernel reads no entry, but the C ABI takes
         # no null pointer (an empty tensor has none)
@@ -431,26 +477,63 @@ def mla_sparse_prepare(indices: torch.Tensor, indptr: torch.Tensor, s_q: int, bl
 def mla_sparse_decode(q: torch.Tensor, kcache: torch.Tensor, offsets: torch.Tensor, indptr: torch.Tensor,
                       counts: torch.Tensor, dv: int, tile_metadata: torch.Tensor, num_splits: torch.Tensor,
                       softmax_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None):
-    """Decode of every query row over its kept cache rows (after mla_sparse_prepare)."""
-    _require(q, "q", torch.bfloat16)
-    _require(kcache, "kcache", torch.bfloat16)
+                      workspace: Optional[torch.Tensor] = None, nnz: Optional[int] = None):
+    """Decode of every query row over its kept cache rows (after mla_sparse_prepare).
+
+    ``nnz`` is the number of index entries (indptr[-1]); the kernel reads up to
+    64 offsets past a row's kept entries, so offsets must hold nnz + 64.  When
+    it is not given it is read from indptr, which synchronises with the device
+    and is refused while a graph is being captured."""
+    _require(q, "q", torch.bfloat16, on_device=False)
+    _require(kcache, "kcache", torch.bfloat16, on_device=False)
     for t, n in ((offsets, "offsets"), (indptr, "indptr"), (counts, "counts"), (tile_metadata, "tile_metadata"),
                  (num_splits, "num_splits")):
-        _require(t, n, torch.int32)
+        _require(t, n, torch.int32, on_device=False)
+    if q.dim() != 4 or kcache.dim() != 4:
+        raise ValueError("q must be [b, s_q, h_q, d] and kcache [pages, 64, h_kv, d]")
     b, s_q, h_q, d_qk = q.shape
     num_pages, page, h_kv, d_k = kcache.shape
-    if d_k != d_qk or h_q % h_kv:
+    if d_k != d_qk or h_kv <= 0 or h_q % h_kv:
         raise ValueError("q / kcache shapes do not match")
+    nq = b * s_q  # every query token is a sequence of its own
+    _shape(indptr, "indptr", (nq + 1,))
+    _shape(counts, "counts", (nq,))
+    _shape(num_splits, "num_splits", (nq + 1,))
+    if tile_metadata.dim() != 2 or tile_metadata.shape[1] != 8 or tile_metadata.shape[0] < 1:
+        raise ValueError(f"tile_metadata must be [num_parts, 8], got {tuple(tile_metadata.shape)}")
+    if offsets.dim() != 1:
+        raise ValueError("offsets must be 1-D")
     rows = h_q // h_kv
     num_parts = tile_metadata.shape[0]
+    if out is not None:
+        _require(out, "out", torch.bfloat16, on_device=False)
+        _shape(out, "out", (b, s_q, h_q, dv))
+    if lse is not None:
+        _require(lse, "lse", torch.float32, on_device=False)
+        _shape(lse, "lse", (b, s_q, h_q))
+    need = (nq + num_parts) * h_kv * rows * (dv + 1) * 4
+    if workspace is not None and workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    def check_nnz(n):
+        if n < 0 or offsets.shape[0] < n + 64:
+            raise ValueError(f"offsets must hold nnz + 64 = {n + 64} entries, got {offsets.shape[0]}")
+
+    if nnz is not None:
+        check_nnz(int(nnz))
     dev = q.device
+    _same_device(dev, q=q, kcache=kcache, offsets=offsets, indptr=indptr, counts=counts,
+                 tile_metadata=tile_metadata, num_splits=num_splits)
+    if nnz is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise ValueError("pass nnz (indptr[-1]) when capturing mla_sparse_decode into a graph")
+        check_nnz(int(indptr[-1].item()))
     if out is None:
         out = torch.empty((b, s_q, h_q, dv), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((b, s_q, h_q), dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = torch.empty((b * s_q + num_parts) * h_kv * rows * (dv + 1) * 4, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _same_device(dev, out=out, lse=lse, workspace=workspace)
     _check(_lib.mla_sparse_decode(q.data_ptr(), kcache.data_ptr(), num_pages, offsets.data_ptr(), indptr.data_ptr(),
                                   counts.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
                                   num_parts, num_splits.data_ptr(), float(softmax_scale), out.data_ptr(),
@@ -471,4 +554,5 @@ def flash_mla_sparse_with_kvcache(q: torch.Tensor, k_cache: torch.Tensor, block_
     h_kv = k_cache.shape[2]
     offsets, counts = mla_sparse_prepare(indices, indptr, s_q, block_table, cache_seqlens, k_cache.shape[0], h_kv)
     md, ns = mla_get_metadata(counts, h_q // h_kv, h_kv, num_parts=num_parts)
-    return mla_sparse_decode(q, k_cache, offsets, indptr, counts, head_dim_v, md, ns, softmax_scale)
+    return mla_sparse_decode(q, k_cache, offsets, indptr, counts, head_dim_v, md, ns, softmax_scale,
+                             nnz=indices.shape[0])
