@@ -6,7 +6,12 @@ exact bf16 input values; it shares no code with the HIP path.
 What it computes, per query head h (d_nope = d_v = 128, latent 512, rope 64):
 
   absorb_q:      q~[t,h,0:512] = sum_n q_nope[t,h,n] W_UK[h,n,:],  q~[t,h,512:] = q_rope[t,h,:]
+  round_bf16:    the bf16 value the decode's query argument holds (round to
+                 nearest, ties to even, from the exact fp64 value)
   unabsorb_out:  out[t,h,v]    = sum_c W_UV[h,v,c] o_lat[t,h,c]
+  bf16_query_chain: absorb_q, round_bf16, the C latent-decode oracle and the
+      up-projection in a row: what the library's absorb -> decode -> unabsorb
+      chain computes up to its own rounding.
   unabsorbed_attention: the MLA attention the two GEMMs and the latent decode
       must reproduce, computed WITHOUT absorption: every head gets its own keys
       k_t = [W_UK[h] c_t ; k_rope_t] and values v_t = W_UV[h] c_t from the cached
@@ -33,6 +38,25 @@ _LATENT = 512
 def _f64(bits: np.ndarray) -> np.ndarray:
     """bf16 bit patterns (uint16) -> float64 (exact)."""
     return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns (uint16), one rounding to nearest with
+    ties to even (bf16 keeps 8 significant bits: 1 implicit + 7 stored).
+
+    x is scaled by a power of two so that its 8 significant bits are the integer
+    part, rounded with numpy's round-half-to-even, and scaled back: every step
+    is exact in fp64.  Values in bf16's normal range only (the layer's queries)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.float64)
+    nz = x != 0
+    e = np.floor(np.log2(np.abs(x[nz])))
+    # guard the floor(log2) of values just below a power of two
+    e = np.where(np.abs(x[nz]) < np.ldexp(1.0, e.astype(np.int64)), e - 1, e)
+    ulp = np.ldexp(1.0, (e - 7).astype(np.int64))
+    out[nz] = np.round(x[nz] / ulp) * ulp
+    f = out.astype(np.float32)  # exact: 8 significant bits
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def absorb_q(q_nope_bits: np.ndarray, q_rope_bits: np.ndarray, w_uk_bits: np.ndarray) -> np.ndarray:
@@ -95,3 +119,50 @@ def unabsorbed_attention(w, layer, scale: Optional[float] = None,
     if sel is None:
         return out.reshape(b, s_q, h_q, -1), lse.reshape(b, s_q, h_q)
     return out, lse
+
+
+def bf16_query_chain(w, layer, sel: Optional[Sequence[int]] = None):
+    """The layer as the decode's ABI runs it: the absorbed query in fp64
+    (absorb_q), rounded to bf16 (round_bf16: the decode takes a bf16 query),
+    the C latent-decode oracle on that query, and the up-projection in fp64.
+
+    Returns (out [n, 128], lse [n], q~ fp64 [b, s_q, h_q, 576]) for all rows
+    (n = b * s_q * h_q) or the flat indices in ``sel``."""
+    import dataclasses
+
+    from oracle import default
+
+    q64 = absorb_q(layer.q_nope, layer.q_rope, layer.w_uk)
+    wq = dataclasses.replace(w, q=round_bf16(q64))
+    o_lat, lse = default().decode(wq, sel=sel)
+    w_uv = _f64(layer.w_uv)
+    rows = np.arange(w.batch * w.s_q * w.h_q) if sel is None else np.asarray(sel, dtype=np.int64)
+    heads = rows % w.h_q
+    out = np.empty((rows.shape[0], w_uv.shape[1]))
+    for h in np.unique(heads):
+        m = heads == h
+        out[m] = o_lat[m] @ w_uv[h].T
+    return out, lse, q64
+
+
+def query_rounding_bound(w, q64: np.ndarray, sel: Sequence[int]) -> np.ndarray:
+    """How far lse may move when every element of the absorbed query q~ is
+    rounded to bf16 (relative change at most 2^-9 per element): each score
+    scale * q~ . K_t moves by at most scale * 2^-9 * sum_i |q~_i K_t,i|, and lse
+    (a log-sum-exp) moves by at most its largest score change.  Per flat row
+    index in ``sel`` over the row's visible keys (0 for a row without keys)."""
+    bound = []
+    cache = {}
+    for idx in sel:
+        b, rem = divmod(int(idx), w.s_q * w.h_q)
+        s, h = divmod(rem, w.h_q)
+        L = int(w.cache_seqlens[b])
+        n = L if not w.causal else max(0, L - w.s_q + s + 1)
+        if n == 0:
+            bound.append(0.0)
+            continue
+        if b not in cache:
+            rows = [w.kcache[w.block_table[b, t // _PAGE], t % _PAGE, 0] for t in range(L)]
+            cache[b] = np.abs(_f64(np.array(rows, dtype=np.uint16).reshape(L, -1)))
+        bound.append(w.scale * 2.0 ** -9 * float(np.max(cache[b][:n] @ np.abs(q64[b, s, h]))))
+    return np.array(bound)

@@ -91,16 +91,14 @@ def test_decode_fp8_small(env, lens, s_q, h_q, h_kv, causal, parts):
     check(go, gl, ro, rl, f"{lens}")
 
 
-def test_decode_fp8_full_size_sampled(env):
+def test_decode_fp8_full_size(env):
+    """memory_bound_varlen over a full-size FP8 cache, every row."""
     _, _, orc, fp8, _, _ = env
     w = workloads.config_workload(1)
     kc8 = workloads.make_fp8_cache(w, seed=1)
     go, gl = decode_fp8(env, w, kc8)
-    rng = np.random.default_rng(11)
-    n = w.batch * w.s_q * w.h_q
-    sel = np.sort(rng.choice(n, size=48, replace=False))
-    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(kc8)), sel=sel)
-    check(go[sel], gl[sel], ro, rl, "memory_bound_varlen fp8")
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(kc8)))
+    check(go, gl, ro, rl, "memory_bound_varlen fp8")
 
 
 @pytest.mark.parametrize("lens,s_q,h_q,h_kv,causal,parts,sexp", [
@@ -127,19 +125,18 @@ def test_decode_fp8_64row_tiles(env, lens, s_q, h_q, h_kv, causal, parts, sexp):
     check(go, gl, ro, rl, f"{lens} rows {s_q * h_q // h_kv}")
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
-def test_decode_fp8_64row_full_size_sampled(env, cfg):
-    """compute_bound_full_heads (128 rows) and long_context (64 rows, ~32 splits
-    per sequence) over FP8 caches of their full size, on sampled rows."""
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_decode_fp8_64row_full_size(env, cfg):
+    """compute_bound_full_heads (128 rows), spec_decode_causal (256 rows, causal)
+    and long_context (64 rows, ~32 splits per sequence) over FP8 caches of their
+    full size, every row."""
     _, _, orc, fp8, _, _ = env
     w = workloads.config_workload(cfg)
     kc8 = workloads.make_fp8_cache(w, seed=cfg)
     go, gl = decode_fp8(env, w, kc8)
-    rng = np.random.default_rng(cfg + 11)
-    n = w.batch * w.s_q * w.h_q
-    sel = np.sort(rng.choice(n, size=32, replace=False))
-    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(kc8)), sel=sel)
-    check(go[sel], gl[sel], ro, rl, f"config {cfg} fp8")
+    w = dataclasses.replace(w, kcache=fp8.bf16_cache(kc8))
+    ro, rl = orc.decode(w)
+    check(go, gl, ro, rl, f"config {cfg} fp8")
 
 
 @pytest.mark.parametrize("lens,s_new,h_kv", [([0, 1, 63, 64, 130], 1, 1), ([5, 62, 200], 3, 2),

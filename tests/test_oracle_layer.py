@@ -94,3 +94,70 @@ def test_layer_identity(oracle_lib, causal, s_q):
     so, sl = mla_layer.unabsorbed_attention(w, lay, sel=sel)
     np.testing.assert_allclose(so, ref_out.reshape(-1, 128)[sel], rtol=0, atol=0)
     assert math.isclose(sl[0], ref_lse.reshape(-1)[0], rel_tol=0, abs_tol=0)
+
+
+def test_round_bf16_hand_values():
+    """bf16 keeps 7 stored mantissa bits: near 1 its spacing is 2^-7, so 1 + 2^-8
+    is a tie (to the even 1.0), 1 + 3*2^-8 a tie between odd 1 + 2^-7 and even
+    1 + 2^-6, and 2 - 2^-9 lies nearer 2 than 2 - 2^-7."""
+    cases = {
+        1.0 + 2.0 ** -8: 0x3F80,
+        1.0 + 3 * 2.0 ** -8: 0x3F82,
+        -(1.0 + 2.0 ** -8): 0xBF80,
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,
+        2.0 - 2.0 ** -9: 0x4000,
+        2.0 - 2.0 ** -7: 0x3FFF,
+        0.0: 0x0000,
+        3.0: 0x4040,
+        2.0 ** -100 * (1 + 2.0 ** -7): 0x0D81,
+    }
+    got = mla_layer.round_bf16(np.array(list(cases.keys())))
+    assert [int(g) for g in got] == list(cases.values())
+
+
+def test_round_bf16_against_fp32_bit_rounding():
+    """On fp32 values (exact in fp64) one rounding to bf16 is the integer
+    round-to-nearest-even of the fp32 bit pattern (workloads.bf16_bits)."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-40, 40, 200000))).astype(np.float32)
+    x[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.5, 2.0 ** -126]
+    assert np.array_equal(mla_layer.round_bf16(x.astype(np.float64)), bf16_bits(x))
+
+
+def test_round_bf16_keeps_bf16_values():
+    rng = np.random.default_rng(6)
+    bits = rng.integers(0x0080, 0x7F80, 50000).astype(np.uint16) | (rng.integers(0, 2, 50000) << 15).astype(np.uint16)
+    assert np.array_equal(mla_layer.round_bf16(f64(bits)), bits)
+
+
+def test_bf16_query_chain_within_the_rounding_bound():
+    """The chain (bf16-rounded absorbed query -> C decode oracle -> up-projection)
+    and the unabsorbed per-head attention differ only by the query's rounding:
+    lse within the derived per-row bound, and the bound is not vacuous (it is
+    small against the lse values and the two results do differ)."""
+    w = make_workload([218, 1, 70], s_q=2, h_q=8, causal=True, seed=41)
+    lay = make_layer_inputs(3, 2, 8, seed=42)
+    n = w.batch * w.s_q * w.h_q
+    out_c, lse_c, q64 = mla_layer.bf16_query_chain(w, lay)
+    out_u, lse_u = mla_layer.unabsorbed_attention(w, lay)
+    out_u, lse_u = out_u.reshape(n, -1), lse_u.reshape(n)
+    bound = mla_layer.query_rounding_bound(w, q64, range(n))
+    fin = np.isfinite(lse_u)
+    assert np.array_equal(fin, np.isfinite(lse_c))
+    diff = np.abs(lse_c[fin] - lse_u[fin])
+    assert np.all(diff <= bound[fin] * (1 + 1e-9))
+    assert 0 < np.max(diff) and np.max(bound) < 0.05
+    rel = np.linalg.norm(out_c - out_u) / np.linalg.norm(out_u)
+    assert 0 < rel < 1e-2
+
+
+def test_truncation_fails_the_rounded_once_bar():
+    """The GPU GEMM bar (at most 1e-3 of the elements one ulp away from the
+    fp64 result rounded to nearest-even) rejects a GEMM that truncates."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(20000) * 0.5
+    rne = mla_layer.round_bf16(x).astype(np.int64)
+    trunc = (np.abs(x).astype(np.float32).view(np.uint32) >> 16).astype(np.int64)  # toward zero, magnitude
+    mag_rne = rne & 0x7FFF
+    frac_off = np.count_nonzero(trunc != mag_rne) / x.size
+    assert frac_off > 0.3
