@@ -60,6 +60,7 @@ extern "C" {
 #define MLA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than mla_plan's size */
 #define MLA_ERR_HIP (-4)         /* a HIP runtime call failed; see mla_last_error() */
 #define MLA_ERR_CAPACITY (-5)    /* page allocator: no free page, or more pages than max_blocks */
+#define MLA_ERR_RANGE (-6)       /* mla_pager_page_owner: page id out of range, or state not initialised */
 
 #define MLA_PAGE_BLOCK_SIZE 64
 #define MLA_D_QK 576
@@ -317,13 +318,15 @@ int mla_sparse_decode(const void* q, const void* kcache, int64_t num_pages, cons
  *   mla_pager_release    return all pages of seq to the pool; its row becomes -1
  *   mla_pager_free_pages number of free pages (or a negative status)
  *   mla_pager_seq_pages  pages held by seq (or a negative status)
- *   mla_pager_page_owner sequence holding a page, -1 if free (or a negative status)
+ *   mla_pager_page_owner sequence holding a page (>= 0), -1 if the page is free,
+ *                        MLA_ERR_RANGE (a distinct value) for a page id outside
+ *                        [0, num_pages) or a state never initialised
  *   mla_pager_block_table pointer to the host block table inside the state
  *                        (NULL if not initialised); copy it to the device for
  *                        mla_kv_append / mla_decode_paged
  * Policy: free pages form a stack (fresh pool: ascending ids; released pages
  * are taken again first).  Errors: MLA_ERR_INVALID, MLA_ERR_WORKSPACE (buffer
- * too small), MLA_ERR_CAPACITY.
+ * too small), MLA_ERR_CAPACITY, MLA_ERR_RANGE.
  */
 size_t mla_pager_bytes(int num_pages, int max_seqs, int max_blocks);
 int mla_pager_init(void* state, size_t bytes, int num_pages, int max_seqs, int max_blocks);

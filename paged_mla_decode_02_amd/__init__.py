@@ -30,6 +30,7 @@ DeepSeek's FlashMLA", deepseekonline.chat, §V.2):
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -45,6 +46,9 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
+# the same library with every page transfer synchronous (a race reference for
+# tests; built beside libmla.so, never used unless selected with library())
+SYNC_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_sync.so")
 PAGE_BLOCK_SIZE = 64
 FP8_ROW_BYTES = 656
 D_QK = 576
@@ -57,12 +61,12 @@ class MlaError(RuntimeError):
         self.code = code
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build the HIP library first "
+            f"{path} is missing: build the HIP library first "
             "(python -m paged_mla_decode_02_amd.build)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.mla_plan.argtypes = [I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(SZ)]
     lib.mla_plan.restype = I
@@ -110,6 +114,22 @@ def _load() -> ctypes.CDLL:
 
 
 _lib = _load()
+_libs = {LIB_PATH: _lib}
+
+
+@contextlib.contextmanager
+def library(path: str):
+    """Calls inside the block go to another build of the library at ``path``
+    (e.g. SYNC_LIB_PATH, the synchronous-transfer reference build)."""
+    global _lib
+    if path not in _libs:
+        _libs[path] = _load(path)
+    prev = _lib
+    _lib = _libs[path]
+    try:
+        yield
+    finally:
+        _lib = prev
 
 
 def _check(rc: int) -> None:

@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmla.so")
+SYNC_LIB_PATH = os.path.join(HERE, "libmla_sync.so")
 SOURCES = ["api.cpp", "pager.cpp", "sched.hip", "decode.hip", "combine.hip", "absorb.hip", "kv_append.hip", "sparse.hip"]
 ARCH = "gfx950"
 
@@ -37,27 +38,40 @@ def common_flags():
             "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + common_flags() + [f"-D{d}" for d in defines] + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, lib_path: str) -> str:
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print(f"built {LIB_PATH}")
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build(verbose: bool = False) -> str:
+    """libmla.so, and libmla_sync.so: the same library with every page transfer
+    synchronous (MLA_SYNC_DEBUG), the reference the race test compares with."""
+    variants = [(LIB_PATH, BUILD_DIR, ()), (SYNC_LIB_PATH, BUILD_DIR + "_sync", ("MLA_SYNC_DEBUG=1",))]
+    jobs = []
+    for _, bdir, defs in variants:
+        os.makedirs(bdir, exist_ok=True)
+        jobs += [(src, bdir, defs) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n = len(SOURCES)
+    for k, (lib_path, _, _) in enumerate(variants):
+        _link(objs[k * n:(k + 1) * n], lib_path)
+        if verbose:
+            print(f"built {lib_path}")
     return LIB_PATH
 
 

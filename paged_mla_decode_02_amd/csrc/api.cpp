@@ -106,7 +106,8 @@ int mla_get_metadata(const int32_t* cache_seqlens, int batch, int rows_per_kv, i
 
 namespace {
 
-enum Stage { kDecode = 1, kCombine = 2 };
+constexpr int kDecode = mla::kStageDecode;
+constexpr int kCombine = mla::kStageCombine;
 
 struct SparseArgs {
   const uint32_t* offsets;
@@ -198,6 +199,17 @@ int decode_common(int stages, int kv_fp8, const SparseArgs* sp, const void* q, c
 }
 
 }  // namespace
+
+int mla::decode_paged_stages(int stages, const void* q, const void* kcache, int64_t num_pages,
+                             const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch,
+                             int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                             const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
+                             float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return decode_common(stages & (kDecode | kCombine), 0, nullptr, q, kcache, num_pages, block_table, max_blocks,
+                       cache_seqlens, batch, s_q, h_q, h_kv, d_qk, dv, page_block_size, tile_metadata, num_parts,
+                       num_splits, causal, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
 
 extern "C" {
 

@@ -242,8 +242,18 @@ __device__ __forceinline__ SliceDma slice_dma_offsets(int tok0, int kvh, int h_k
 // register result.  M0 holds the LDS base; one wait state separates its write
 // from the transfer that reads it.  The immediate offset would move the LDS
 // destination as well, so the source offset is all in voffset.
+// MLA_SYNC_DEBUG (a separate reference build of the library, never the
+// product path): every transfer waits for itself right after it is issued, so
+// no page data is ever in flight while the kernel runs on.  Its results must be
+// bit-identical to the pipelined build's; a wait miscounted in the pipeline
+// would show up as a difference.
+#ifdef MLA_SYNC_DEBUG
+#define MLA_DMA_TAIL "\n\ts_waitcnt vmcnt(0)"
+#else
+#define MLA_DMA_TAIL ""
+#endif
 __device__ __forceinline__ void dma16(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" MLA_DMA_TAIL
                :
                : "s"((unsigned)(size_t)dst), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
@@ -341,7 +351,7 @@ __device__ __forceinline__ void dequant_slice(const LDS_AS char* src, LDS_AS cha
 // with the page transfers, and each lane then reads the offsets of its two
 // tokens: no registers hold a page's offsets while it is in flight.
 __device__ __forceinline__ void dma4(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" MLA_DMA_TAIL
                :
                : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)dst)), "v"(voffset), "s"(rsrc)
                : "memory", "m0");

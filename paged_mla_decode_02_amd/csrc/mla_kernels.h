@@ -64,6 +64,18 @@ constexpr uint32_t kSparseMaxCacheBytes = 0xE0000000u;
 // mla_last_error) and returns `code`.
 int set_status(int code, const char* msg);
 
+// The bf16 paged decode behind mla_decode_paged: validates every argument on
+// the host, then enqueues the stages in `stages` (kStageDecode | kStageCombine;
+// 0 validates only and launches nothing).  Status as the C ABI.
+constexpr int kStageDecode = 1;
+constexpr int kStageCombine = 2;
+int decode_paged_stages(int stages, const void* q, const void* kcache, int64_t num_pages,
+                        const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens, int batch,
+                        int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                        const int32_t* tile_metadata, int num_parts, const int32_t* num_splits, int causal,
+                        float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int rows, int num_parts,
                            int32_t* tile_md, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

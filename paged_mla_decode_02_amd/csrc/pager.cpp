@@ -127,8 +127,9 @@ int mla_pager_seq_pages(const void* state, int seq) {
 
 int mla_pager_page_owner(const void* state, int page) {
   Header* h = state_of(const_cast<void*>(state));
-  if (!h) return pager_fail(MLA_ERR_INVALID, "pager: state not initialised");
-  if (page < 0 || page >= h->num_pages) return pager_fail(MLA_ERR_INVALID, "pager: page id out of range");
+  // -1 means "free" here, so errors use a status that no owner value takes
+  if (!h) return pager_fail(MLA_ERR_RANGE, "pager: state not initialised");
+  if (page < 0 || page >= h->num_pages) return pager_fail(MLA_ERR_RANGE, "pager: page id out of range");
   return owner(h)[page];
 }
 

@@ -235,3 +235,4 @@ def test_sparse_decode_rejects(lib, over, code):
                                       ctypes.c_float, P, P, P, SZ, P]
     assert lib.mla_sparse_decode(*sparse_decode_args(**over)) == code
     assert lib.mla_last_error()
+

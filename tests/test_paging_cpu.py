@@ -14,7 +14,7 @@ import pytest
 from oracle import paging
 from workloads import make_append_case
 
-MLA_ERR_INVALID, MLA_ERR_WORKSPACE, MLA_ERR_CAPACITY = -1, -3, -5
+MLA_ERR_INVALID, MLA_ERR_WORKSPACE, MLA_ERR_CAPACITY, MLA_ERR_RANGE = -1, -3, -5, -6
 
 
 def test_pages_needed_closed_form():
@@ -125,8 +125,20 @@ def test_pager_rejects_bad_calls(mla):
     assert lib.mla_pager_reserve(p, 2, 10) == MLA_ERR_INVALID
     assert lib.mla_pager_reserve(p, 0, -1) == MLA_ERR_INVALID
     assert lib.mla_pager_reserve(p, 0, 129) == MLA_ERR_CAPACITY  # 3 pages > max_blocks 2
-    assert lib.mla_pager_page_owner(p, 4) == MLA_ERR_INVALID
+    assert lib.mla_pager_page_owner(p, 4) == MLA_ERR_RANGE  # distinct from -1 (= free)
+    assert lib.mla_pager_page_owner(p, -1) == MLA_ERR_RANGE
     assert lib.mla_pager_release(p, -1) == MLA_ERR_INVALID
     assert lib.mla_pager_reserve(p, 0, 128) == 0 and lib.mla_pager_reserve(p, 1, 128) == 0
     assert lib.mla_pager_free_pages(p) == 0
     assert lib.mla_pager_reserve(p, 1, 128) == 0  # already held
+
+
+def test_page_owner_out_of_range_raises():
+    """An out-of-range page id is an error, not the -1 of a free page."""
+    import paged_mla_decode_02_amd as mla
+    pg = mla.Pager(8, 2, 4)
+    assert pg.page_owner(3) == -1
+    with pytest.raises(mla.MlaError):
+        pg.page_owner(8)
+    with pytest.raises(mla.MlaError):
+        pg.page_owner(-1)
