@@ -141,6 +141,29 @@ int mla_decode_paged(const void* q, const void* kcache, int64_t num_pages,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_paged_noalloc -- mla_decode_paged for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments without the workspace; same kernels
+ * and results.  The split partials go into a fixed array of the library in
+ * device memory, MLA_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library
+ * runs on holds until the process ends.  The call allocates nothing (no
+ * hipMalloc, no library allocation); the caller still owns every input and
+ * output.  A call needing more than the array,
+ *   (batch + num_parts) * h_kv * rows_per_kv * (dv + 1) * 4 bytes,
+ * returns MLA_ERR_WORKSPACE before any HIP call.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap on a GPU (other streams or threads)
+ * race and must be serialised by the caller.  The first call on a device looks
+ * up the array's address there (hipGetSymbolAddress).
+ * Errors: as mla_decode_paged.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (256u << 20)
+int mla_decode_paged_noalloc(const void* q, const void* kcache, int64_t num_pages,
+                             const int32_t* block_table, int max_blocks, const int32_t* cache_seqlens,
+                             int batch, int s_q, int h_q, int h_kv, int d_qk, int dv, int page_block_size,
+                             const int32_t* tile_metadata, int num_parts, const int32_t* num_splits,
+                             int causal, float softmax_scale, void* out, float* lse, void* stream);
+
+/*
  * The two stages of mla_decode_paged as separate calls, same arguments and
  * errors.  mla_decode_splitkv enqueues the decode kernel only: sequences kept
  * in one chunk get out/lse, split sequences leave fp32 partials in `workspace`.

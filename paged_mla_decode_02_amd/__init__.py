@@ -42,7 +42,7 @@ __all__ = [
     "mla_decode_splitkv", "mla_combine_splits", "get_mla_metadata", "flash_mla_with_kvcache",
     "mla_absorb_q", "mla_unabsorb_out", "mla_kv_append", "Pager", "mla_decode_paged_fp8",
     "mla_decode_splitkv_fp8", "FP8_ROW_BYTES", "mla_sparse_prepare", "mla_sparse_decode",
-    "flash_mla_sparse_with_kvcache",
+    "flash_mla_sparse_with_kvcache", "mla_decode_paged_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla.so")
@@ -53,6 +53,7 @@ PAGE_BLOCK_SIZE = 64
 FP8_ROW_BYTES = 656
 D_QK = 576
 DV = 512
+NOALLOC_SCRATCH_BYTES = 256 << 20  # MLA_NOALLOC_SCRATCH_BYTES of include/mla.h
 
 
 class MlaError(RuntimeError):
@@ -80,6 +81,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
                        ctypes.c_float, P, P, P, SZ, P]
         fn.restype = I
+    lib.mla_decode_paged_noalloc.argtypes = [P, P, ctypes.c_int64, P, I, P, I, I, I, I, I, I, I, P, I, P, I,
+                                             ctypes.c_float, P, P, P]
+    lib.mla_decode_paged_noalloc.restype = I
     lib.mla_absorb_q.argtypes = [P, P, P, I, I, P, P]
     lib.mla_absorb_q.restype = I
     lib.mla_unabsorb_out.argtypes = [P, P, I, I, P, P]
@@ -272,6 +276,44 @@ def mla_decode_paged(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.T
     """Paged decode; returns (out bf16 [b, s_q, h_q, dv], lse fp32 [b, s_q, h_q])."""
     return _decode_call(_lib.mla_decode_paged, q, kcache, block_table, cache_seqlens, dv, tile_metadata,
                         num_splits, causal, softmax_scale, out, lse, workspace)
+
+
+def mla_decode_paged_noalloc(q: torch.Tensor, kcache: torch.Tensor, block_table: torch.Tensor,
+                             cache_seqlens: torch.Tensor, dv: int, tile_metadata: torch.Tensor,
+                             num_splits: torch.Tensor, causal: bool, softmax_scale: float,
+                             out: torch.Tensor, lse: torch.Tensor):
+    """mla_decode_paged without a workspace and without allocating: the split
+    partials use the library's fixed per-GPU scratch array (at most
+    NOALLOC_SCRATCH_BYTES).  ``out`` and ``lse`` are the caller's.  Calls that
+    overlap on one GPU race on that array."""
+    for t, n, dt in ((q, "q", torch.bfloat16), (kcache, "kcache", torch.bfloat16),
+                     (block_table, "block_table", torch.int32), (cache_seqlens, "cache_seqlens", torch.int32),
+                     (tile_metadata, "tile_metadata", torch.int32), (num_splits, "num_splits", torch.int32),
+                     (out, "out", torch.bfloat16), (lse, "lse", torch.float32)):
+        _require(t, n, dt, on_device=False)
+    if q.dim() != 4 or kcache.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q must be [b, s_q, h_q, d], kcache [pages, 64, h_kv, d], block_table [b, n]")
+    b, s_q, h_q, d_qk = q.shape
+    num_pages, page, h_kv, d_k = kcache.shape
+    if d_k != d_qk or h_kv <= 0 or h_q % h_kv:
+        raise ValueError("q / kcache shapes do not match")
+    if block_table.shape[0] != b:
+        raise ValueError(f"block_table must have one row per sequence ({b}), got {block_table.shape[0]}")
+    _shape(cache_seqlens, "cache_seqlens", (b,))
+    _shape(num_splits, "num_splits", (b + 1,))
+    if tile_metadata.dim() != 2 or tile_metadata.shape[1] != 8 or tile_metadata.shape[0] < 1:
+        raise ValueError(f"tile_metadata must be [num_parts, 8], got {tuple(tile_metadata.shape)}")
+    _shape(out, "out", (b, s_q, h_q, dv))
+    _shape(lse, "lse", (b, s_q, h_q))
+    dev = q.device
+    _same_device(dev, q=q, kcache=kcache, block_table=block_table, cache_seqlens=cache_seqlens,
+                 tile_metadata=tile_metadata, num_splits=num_splits, out=out, lse=lse)
+    _check(_lib.mla_decode_paged_noalloc(
+        q.data_ptr(), kcache.data_ptr(), num_pages, block_table.data_ptr(), block_table.shape[1],
+        cache_seqlens.data_ptr(), b, s_q, h_q, h_kv, d_qk, dv, page, tile_metadata.data_ptr(),
+        tile_metadata.shape[0], num_splits.data_ptr(), int(bool(causal)), float(softmax_scale),
+        out.data_ptr(), lse.data_ptr(), _stream(dev)))
+    return out, lse
 
 
 def mla_decode_splitkv(q, kcache, block_table, cache_seqlens, dv, tile_metadata, num_splits, causal,

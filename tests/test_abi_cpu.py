@@ -236,3 +236,30 @@ def test_sparse_decode_rejects(lib, over, code):
     assert lib.mla_sparse_decode(*sparse_decode_args(**over)) == code
     assert lib.mla_last_error()
 
+
+def noalloc_args(**over):
+    a = dict(q=FAKE, kc=FAKE, np_=100, bt=FAKE, mb=8, sl=FAKE, b=64, s_q=1, h_q=16, h_kv=1, d_qk=576, dv=512,
+             page=64, md=FAKE, P=256, ns=FAKE, causal=0, scale=0.07, out=FAKE, lse=FAKE, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), MLA_ERR_INVALID),
+    (dict(d_qk=512), MLA_ERR_UNSUPPORTED),
+    (dict(h_q=17, h_kv=2), MLA_ERR_INVALID),
+    # (8192 + 256) * 256 rows * 513 * 4 bytes is far above the 256 MiB array
+    (dict(b=8192, s_q=2, h_q=128), MLA_ERR_WORKSPACE),
+    (dict(b=600, s_q=2, h_q=128), MLA_ERR_WORKSPACE),
+])
+def test_decode_noalloc_rejects(lib, over, code):
+    """Validation, including the scratch limit, runs before any HIP call."""
+    lib.mla_decode_paged_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int] * 7 + [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.mla_decode_paged_noalloc(*noalloc_args(**over)) == code
+    msg = lib.mla_last_error().decode()
+    assert msg
+    if code == MLA_ERR_WORKSPACE:
+        assert "268435456" in msg and "scratch" in msg
