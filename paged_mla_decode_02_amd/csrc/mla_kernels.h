@@ -23,8 +23,11 @@ constexpr int kF8Group = 128;
 constexpr int kF8RowBytes = kLatent + 4 * (kLatent / kF8Group) + 2 * kRope;
 
 // Query rows one workgroup owns: <= 16 rows use the 16-row token-split kernel,
-// larger row counts the 64-row pair-split kernel (ceil(rows / 64) row tiles).
-__host__ __device__ constexpr int tile_rows_for(int rows) { return rows <= 16 ? 16 : 64; }
+// up to 64 rows the 64-row pair-split kernel, more the 128-row kernel
+// (ceil(rows / 128) row tiles).  The FP8 and token-sparse decodes keep 64-row
+// tiles for any row count (pair_tiles_for).
+__host__ __device__ constexpr int tile_rows_for(int rows) { return rows <= 16 ? 16 : rows <= 64 ? 64 : 128; }
+__host__ __device__ constexpr int pair_tiles_for(int rows) { return (rows + 63) / 64; }
 // Fixed per-chunk cost, in page units, that the scheduler charges before each
 // sequence: loading the query tile, the end-of-chunk merge and writing /
 // re-reading a split partial.  The 16-row token-split kernel's chunk end (a merge
@@ -79,6 +82,7 @@ int decode_paged_stages(int stages, const void* q, const void* kcache, int64_t n
 hipError_t launch_metadata(const int32_t* seqlens, int batch, int rows, int num_parts,
                            int32_t* tile_md, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int tokens,
                            int h_q, uint16_t* q_abs, hipStream_t stream);
