@@ -337,15 +337,15 @@ def bench_append(args, torch, mla, workloads, dev):
 
 
 def bench_sparse(args, torch, mla, workloads, dev):
-    """Token-sparse decode: 64 sequences of U[4096, 16384] tokens, 128 query
-    heads, each query attending to a top-2048 selection (uniform distinct
-    positions).  A step is the decode of the kept rows (decode + combine),
+    """Token-sparse decode: 64 sequences of U[4096, 16384] tokens, --sparse-heads
+    query heads (128 by default; 16 is one GPU's eighth of a 128-head model),
+    each query attending to a top-2048 selection (uniform distinct positions).  A step is the decode of the kept rows (decode + combine),
     replayed from graphs of consecutive steps; the preparation (list -> row offsets) and the schedule run
     once per step in use and are timed on their own."""
     import numpy as np
     rng = np.random.default_rng(20)
     lens = rng.integers(4096, 16385, size=64)
-    w = workloads.make_workload(lens, s_q=1, h_q=128, seed=20, name="sparse_topk2048")
+    w = workloads.make_workload(lens, s_q=1, h_q=args.sparse_heads, seed=20, name="sparse_topk2048")
     idx, ptr = workloads.make_sparse_indices(w, args.topk, seed=20)
     q = torch.from_numpy(w.q.view(np.int16)).to(dev).view(torch.bfloat16)
     kc_host = torch.from_numpy(w.kcache.view(np.int16))
@@ -423,6 +423,7 @@ def main():
     ap.add_argument("--append-tokens", type=int, default=0,
                     help="--op append: rows appended per sequence (default: the workload's s_q)")
     ap.add_argument("--topk", type=int, default=2048, help="--op sparse: entries selected per query")
+    ap.add_argument("--sparse-heads", type=int, default=128, help="--op sparse: query heads (one KV head)")
     ap.add_argument("--op", choices=["decode", "absorb", "append", "sparse"], default="decode",
                     help="decode (default): the decode step; absorb: the two absorption GEMMs of the "
                          "workload's query tokens and heads (one JSON line of their own)")

@@ -155,19 +155,21 @@ __device__ __forceinline__ SliceDma gathered_dma(const LDS_AS char* staged, int 
 // cache the slots hold FP8 images (2 x 10496 B) and a third region holds the
 // dequantised bf16 slice the wave computes on.  At a chunk end the waves merge
 // their partial outputs through the slot just consumed.
-template <bool kFp8>
+template <bool kFp8, bool kSparse = false>
 struct TsLayout {
   static constexpr int kSlot = kFp8 ? kF8SliceBytes : kSliceBytes;
   static constexpr int kWave = kFp8 ? 2 * kF8SliceBytes + kSliceBytes : 2 * kSliceBytes;
   static constexpr int kDma = kFp8 ? kF8SliceDma : kSliceDma;  // transfers per slice issue
   static constexpr int kStat = 4 * kWave;                        // [4 waves][16 rows][m, l]
-  static constexpr int kLds = kStat + 4 * 16 * 2 * 4;
+  static constexpr int kOffs = kStat + 4 * 16 * 2 * 4;          // token-sparse: [4 waves][2 pages][16] row offsets
+  static constexpr int kLds = kOffs + (kSparse ? 4 * 2 * kSlice * 4 : 0);
 };
 
-template <bool kFp8>
+template <bool kFp8, bool kSparse = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_tokensplit(DecodeParams p) {
-  using Lay = TsLayout<kFp8>;
+  static_assert(!(kSparse && kFp8), "the token-sparse decode reads bf16 rows");
+  using Lay = TsLayout<kFp8, kSparse>;
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
   const int lane = threadIdx.x & 63;
@@ -207,6 +209,29 @@ decode_tokensplit(DecodeParams p) {
     if constexpr (kFp8) dma_slice_fp8(dst, page_rsrc(p, page_id(ids_, k), blk_, r.L, kF8RowBytes), f8dma, lane);
     else dma_slice(dst, page_rsrc(p, page_id(ids_, k), blk_, r.L), dma);
   };
+  // Token-sparse: a sequence's rows are listed, not paged.  The offsets of the
+  // slice of page n of a chunk sit in this wave's LDS slot n & 1: staged two
+  // pages ahead, each just before the transfer of the page in between, so the
+  // wait that covers a slice also covers the offsets staged before its
+  // successor's transfer.  A sequence's first page is requested when the
+  // sequence starts, not during its predecessor.
+  i32x4_t grsrc = {}, offs_rsrc = {};
+  if constexpr (kSparse) {
+    grsrc = make_rsrc(p.kcache, p.sp_cache_bytes);
+    offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);
+  }
+  LDS_AS char* offs_slot = smem + Lay::kOffs + w * 2 * kSlice * 4;
+  const auto slice_valid = [&](const SeqRange& r, int blk_) {
+    return min(max(r.L - blk_ * kPage - w * kSlice, 0), kSlice);
+  };
+  int row0 = 0;  // token-sparse: the current sequence's first entry in the offset list
+  auto sparse_start = [&](LDS_AS char* dst, int bq, const SeqRange& r) {
+    row0 = ((const CONST_AS int32_t*)p.sp_rowptr)[bq];
+    stage_offs(offs_slot, offs_rsrc, row0, r.lo, w, lane);
+    if (r.lo + 1 < r.hi) stage_offs(offs_slot + kSlice * 4, offs_rsrc, row0, r.lo + 1, w, lane);
+    wait_vmcnt<0>();
+    dma_slice(dst, grsrc, gathered_dma(offs_slot, slice_valid(r, r.lo), kvh, lane));
+  };
 
   // queries: B operand of the 16x16x32 QK MFMA, 8 dims per lane per k-step.
   // Rows past the last one (a ragged tile) compute on row 0's query; every row
@@ -243,7 +268,10 @@ decode_tokensplit(DecodeParams p) {
     ids = load_page_ids(p, b, sr.lo, lane);
     vm_drain();
   }
-  if (sr.lo < sr.hi) issue(slices, ids, 0, sr.lo, sr);
+  if (sr.lo < sr.hi) {
+    if constexpr (kSparse) sparse_start(slices, b, sr);
+    else issue(slices, ids, 0, sr.lo, sr);
+  }
   for (;;) {
     const bool has_next = b < j0;
     SeqDesc nd2 = {};
@@ -264,12 +292,18 @@ decode_tokensplit(DecodeParams p) {
 
     bool next_started = false;  // first page of the next sequence already requested
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
-      if (blk + 1 < sr.hi) {
+      if (kSparse && blk + 1 < sr.hi) {
+        const int n0 = blk - sr.lo;
+        if (blk + 2 < sr.hi) stage_offs(offs_slot + (n0 & 1) * kSlice * 4, offs_rsrc, row0, blk + 2, w, lane);
+        dma_slice(slices + (buf ^ 1) * Lay::kSlot, grsrc,
+                  gathered_dma(offs_slot + ((n0 + 1) & 1) * kSlice * 4, slice_valid(sr, blk + 1), kvh, lane));
+        wait_vmcnt<Lay::kDma>();
+      } else if (blk + 1 < sr.hi) {
         const int k = (blk + 1 - sr.lo) & 63;
         if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
         issue(slices + (buf ^ 1) * Lay::kSlot, ids, k, blk + 1, sr);
         wait_vmcnt<Lay::kDma>();
-      } else if (has_next && nr.lo < nr.hi) {
+      } else if (!kSparse && has_next && nr.lo < nr.hi) {
         issue(slices + (buf ^ 1) * Lay::kSlot, nids, 0, nr.lo, nr);
         next_started = true;
         wait_vmcnt<Lay::kDma>();
@@ -468,7 +502,10 @@ decode_tokensplit(DecodeParams p) {
     ids = nids;
     nr = seq_range(p, nd2, b + 1, i0, f0, j0, e0, ord0);
     nids = nids2;
-    if (!next_started && sr.lo < sr.hi) issue(slices + buf * Lay::kSlot, ids, 0, sr.lo, sr);
+    if (!next_started && sr.lo < sr.hi) {
+      if constexpr (kSparse) sparse_start(slices + buf * Lay::kSlot, b, sr);
+      else issue(slices + buf * Lay::kSlot, ids, 0, sr.lo, sr);
+    }
   }
 }
 
@@ -1014,7 +1051,8 @@ hipError_t launch_one(int lds, const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  if (tile_rows_for(p.rows) == 16 && !p.sparse) {
+  if (tile_rows_for(p.rows) == 16) {
+    if (p.sparse) return launch_one<decode_tokensplit<false, true>>(TsLayout<false, true>::kLds, p, stream);
     if (p.kv_fp8) return launch_one<decode_tokensplit<true>>(TsLayout<true>::kLds, p, stream);
     return launch_one<decode_tokensplit<false>>(TsLayout<false>::kLds, p, stream);
   }

@@ -243,6 +243,46 @@ __device__ __forceinline__ void dma_slice(LDS_AS char* dst, i32x4_t rsrc, const 
   dma_groups(dst, rsrc, d, std::make_integer_sequence<int, 9>{});
 }
 
+// P tiles of the half-page kernels: row r holds 32 bf16 tokens as 4 chunks of
+// 16 bytes; chunk c sits at position c ^ ((r >> 2) & 3), so the 16 rows a
+// quarter wave reads with one 16-byte read fall on 16 distinct bank groups.
+__device__ __forceinline__ int wp_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// PV accumulation in AGPRs (the 128-row kernel):
+// O^T += V^T . P^T as inline assembly accumulating in AGPRs, while the
+// compiler's own MFMAs (QK^T) accumulate the scores in VGPRs next to the
+// queries.  O is only ever touched through the statements below (all with the
+// AGPR operand class, all updating in place), so it keeps the AGPR file and
+// the compiler cannot spill into it.  Wait states the compiler cannot see
+// inside the assembly are written out: one before each MFMA (a VALU write of
+// an operand), 20 before O is read by VALU instructions (an MFMA result), 4
+// after O is written by VALU instructions and before an MFMA accumulates on it.
+__device__ __forceinline__ void pv_mfma(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void acc_zero(f32x16_t& acc) { asm volatile("s_nop 3" : "=a"(acc) : "0"(f32x16_t{})); }
+__device__ __forceinline__ void acc_settle(f32x16_t& acc) { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+a"(acc)); }
+// acc *= s in place, one element at a time through a VGPR (the caller settles
+// the tuple before and waits 4 states after)
+__device__ __forceinline__ void acc_scale(f32x16_t& acc, float s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float e = acc[i];
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(e), "=&v"(t)
+                 : "v"(s));
+    acc[i] = e;
+  }
+}
+// O tuple -> VGPRs (after the MFMA result wait)
+__device__ __forceinline__ f32x16_t acc_out(f32x16_t& acc) {
+  acc_settle(acc);
+  f32x16_t t;
+  asm volatile("" : "=v"(t) : "0"(acc));
+  return t;
+}
+
 __device__ __forceinline__ void row_coords(const DecodeParams& p, int b, int kvh, int row, int& s,
                                            long long& qo) {
   s = row / p.group;

@@ -66,6 +66,11 @@ def test_prepare_bit_exact(env, lens, s_q, h_kv, topk, invalid):
     ([300, 70, 1000, 5], 2, 64, 1, 200, 0.3, (3,), None),
     ([2500, 900], 1, 128, 1, 1000, 0.0, (), 9),      # two row tiles, forced splits
     ([640, 33], 2, 32, 2, 130, 0.1, (0,), None),
+    # <= 16 rows per KV head (the 16-row kernel's gathered slices): many pages
+    # per row, several rows per part, forced splits, ragged 8- and 12-row tiles
+    ([5000, 3, 64, 129, 2000], 2, 16, 1, 1500, 0.1, (1,), 3),
+    ([4100, 700], 1, 8, 1, 1400, 0.0, (), None),
+    ([3000, 65, 1, 2048], 3, 24, 2, 700, 0.2, (4,), 7),
 ])
 def test_sparse_decode_small(env, lens, s_q, h_q, h_kv, topk, invalid, empty, parts):
     torch, mla, sparse, dev = env
