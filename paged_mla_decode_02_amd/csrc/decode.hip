@@ -40,9 +40,9 @@
 //     resident in registers), P goes through LDS, and PV is split by output dims
 //     (128 per wave), so each V element of a page is read from LDS once per
 //     workgroup.
-// Both also run on the FP8 cache (656-byte rows, see kF8RowBytes): the 16-row
-// kernel dequantises each slice in LDS, the 64-row kernel keeps FP8 pages in
-// LDS and dequantises its MFMA operands in registers.
+// Both also run on the FP8 cache (656-byte rows, see kF8RowBytes): pages stay
+// FP8 in LDS and the MFMA operands are dequantised in registers, K with its
+// per-group scale and V without, the V scale folded into P.
 #include <type_traits>
 #include <utility>
 
@@ -53,9 +53,9 @@ namespace {
 
 // FP8 cache (656-byte rows, see kF8RowBytes).  A 16-token slice moves as 656
 // token-major 16-byte chunks: 10 full transfers and one of 16 lanes; lane i of
-// transfer k supplies chunk 64k + i.  Its LDS image is dequantised into the
-// bf16 slice layout above before the slice is used, so the scoring and PV code
-// is the same for both formats.
+// transfer k supplies chunk 64k + i, so the LDS image is the slice's rows one
+// after the other.  The kernels read their MFMA operands from that image and
+// dequantise them in registers.
 constexpr int kF8SliceBytes = kSlice * kF8RowBytes;             // 10496
 constexpr int kF8Chunks = kF8RowBytes / 16;                     // 41 per row
 constexpr int kF8SliceDma = (kF8SliceBytes + 1023) / 1024;      // 11
@@ -84,35 +84,24 @@ __device__ __forceinline__ unsigned cvt_fp8x2(unsigned v, float scale, bool hi_w
   return hi_word ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, true))
                  : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, false));
 }
-// FP8 slice image (token-major rows) -> bf16 slice (swizzled).  Lane l takes
-// token l%16 and latent group l/16: 128 dims with that group's scale, plus rope
-// dims 16(l/16) .. +15 copied as they are.  With the token in the low lane bits
-// the 16 lanes of a group read 16 distinct 16-byte bank groups (rows are 656 =
-// 144 mod 256 bytes apart) and write 16 distinct ones (the slice swizzle).
-__device__ __forceinline__ void dequant_slice(const LDS_AS char* src, LDS_AS char* dst, int lane) {
-  const int t = lane & 15, g = lane >> 4;
-  const LDS_AS char* row = src + t * kF8RowBytes;
-  // every read first, so that one LDS round trip covers them all
-  u32x4_t v[8], rope[2];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) v[c] = *(const LDS_AS u32x4_t*)(row + g * kF8Group + 16 * c);
-#pragma unroll
-  for (int c = 0; c < 2; ++c) rope[c] = *(const LDS_AS u32x4_t*)(row + kLatent + 16 + 32 * g + 16 * c);
-  const float sc = *(const LDS_AS float*)(row + kLatent + 4 * g);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const u32x4_t lo = {cvt_fp8x2(v[c][0], sc, false), cvt_fp8x2(v[c][0], sc, true), cvt_fp8x2(v[c][1], sc, false),
-                        cvt_fp8x2(v[c][1], sc, true)};
-    const u32x4_t hi = {cvt_fp8x2(v[c][2], sc, false), cvt_fp8x2(v[c][2], sc, true), cvt_fp8x2(v[c][3], sc, false),
-                        cvt_fp8x2(v[c][3], sc, true)};
-    *(LDS_AS u32x4_t*)(dst + slice_off(t, 16 * g + 2 * c)) = lo;
-    *(LDS_AS u32x4_t*)(dst + slice_off(t, 16 * g + 2 * c + 1)) = hi;
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) *(LDS_AS u32x4_t*)(dst + slice_off(t, 64 + 2 * g + c)) = rope[c];
+// 8 e4m3 codes (two words) -> 8 bf16 times a power-of-two scale (exact)
+__device__ __forceinline__ bf16x8_t cvt8_fp8(unsigned w0, unsigned w1, float sc) {
+  const u32x4_t r = {cvt_fp8x2(w0, sc, false), cvt_fp8x2(w0, sc, true), cvt_fp8x2(w1, sc, false),
+                     cvt_fp8x2(w1, sc, true)};
+  return __builtin_bit_cast(bf16x8_t, r);
 }
-
+// 8 bf16 values, element j times sc[j] (powers of two: exact while the
+// products stay in bf16's normal range)
+__device__ __forceinline__ bf16x8_t scale8(bf16x8_t v, const float* sc) {
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_bf16(__builtin_bit_cast(float, u[i] << 16) * sc[2 * i],
+                     __builtin_bit_cast(float, u[i] & 0xffff0000u) * sc[2 * i + 1]);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 // Token-sparse decode.  A wave's 16-token slice of page blk of sequence b is
 // rows sp_offs[sp_rowptr[b] + 64 blk + 16 w + t], t < 16 (byte offsets; the
 // array is padded by one page, so a last page's reads stay inside it).  The 16
@@ -152,9 +141,10 @@ __device__ __forceinline__ SliceDma gathered_dma(const LDS_AS char* staged, int 
 // length and page ids load while the current one runs, its queries during the
 // current one's epilogue.
 // LDS: per wave two 16-token transfer slots + merge statistics; with the FP8
-// cache the slots hold FP8 images (2 x 10496 B) and a third region holds the
-// dequantised bf16 slice the wave computes on.  At a chunk end the waves merge
-// their partial outputs through the slot just consumed.
+// cache the slots hold FP8 images (2 x 10496 B), too small for a wave's partial
+// output, so a third region of 18 KB takes the chunk-end merge.  At a chunk end
+// the waves merge their partial outputs through the slot just consumed (bf16)
+// or that region (FP8).
 template <bool kFp8, bool kSparse = false>
 struct TsLayout {
   static constexpr int kSlot = kFp8 ? kF8SliceBytes : kSliceBytes;
@@ -182,7 +172,6 @@ decode_tokensplit(DecodeParams p) {
   if (i0 >= p.batch || i0 < 0) return;
 
   LDS_AS char* slices = smem + w * Lay::kWave;                     // transfer slot k at k * Lay::kSlot
-  LDS_AS char* bslice = smem + w * Lay::kWave + 2 * kF8SliceBytes;  // FP8 only: dequantised slice
   LDS_AS float* mstat = (LDS_AS float*)(smem + Lay::kStat);         // [4 waves][16 rows][2]
 
   // lane roles: QK output / PV operand B -> query row (lane & 15)
@@ -311,16 +300,43 @@ decode_tokensplit(DecodeParams p) {
         wait_vmcnt<0>();
       }
       const LDS_AS char* reg = slices + buf * Lay::kSlot;
-      if constexpr (kFp8) {
-        dequant_slice(reg, bslice, lane);
-        reg = bslice;
-      }
 
       // S^T[16 tokens x 16 rows] = K_slice . Q^T ; A-operand row = token r16,
       // chunk 4*ks + grp = group ks/2, position 4*(ks&1) + grp.  Three
       // accumulation chains; K operands are read kAhead k-steps ahead.
       f32x4_t S;
-      {
+      if constexpr (kFp8) {
+        // FP8 rows, read where they landed (token-major, 656 bytes): a latent
+        // k-step is 8 e4m3 codes of token r16, converted with the token's
+        // scale of that 128-dim group (exact: powers of two); rope k-steps are
+        // bf16 already.  Raw operands are read kAhead k-steps ahead and
+        // converted just before their MFMA.
+        const LDS_AS char* krow = reg + r16 * kF8RowBytes;
+        const f32x4_t ksc = *(const LDS_AS f32x4_t*)(krow + kLatent);
+        auto kraw = [&](int n) {
+          if (n < 16) {
+            const u32x2_t v = *(const LDS_AS u32x2_t*)(krow + 32 * n + 8 * grp);
+            return u32x4_t{v[0], v[1], 0u, 0u};
+          }
+          return *(const LDS_AS u32x4_t*)(krow + kLatent + 16 + 64 * (n - 16) + 16 * grp);
+        };
+        constexpr int kAhead = 4;
+        f32x4_t Sc[3] = {};
+        u32x4_t kr[kAhead + 1];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) kr[i] = kraw(i);
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+          if (ks + kAhead < 18) kr[(ks + kAhead) % (kAhead + 1)] = kraw(ks + kAhead);
+          const u32x4_t c = kr[ks % (kAhead + 1)];
+          const bf16x8_t ka = ks < 16 ? cvt8_fp8(c[0], c[1], ksc[ks >> 2]) : __builtin_bit_cast(bf16x8_t, c);
+          Sc[ks % 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[ks], Sc[ks % 3], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100 | 0x002, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        S = Sc[0] + Sc[1] + Sc[2];
+      } else {
         constexpr int kAhead = 4;
         f32x4_t Sc[3] = {};
         bf16x8_t ka[kAhead + 1];
@@ -376,7 +392,45 @@ decode_tokensplit(DecodeParams p) {
       // O^T[16 dims x 16 rows] += V^T[16 dims x 16 tokens] . P^T, 32 dim tiles;
       // dims 16*dt + (lane&3)*4 = group dt/4, position 2*(dt&3) + (lane&3)/2.
       // Transposed reads run kVAhead tiles ahead of their MFMA.
-      {
+      if constexpr (kFp8) {
+        // V^T through the 8-bit transposed read: the 16 lanes of a group
+        // address tokens 8 (grp >> 1) + (r16 >> 1) at bytes 16 dt + 8 (r16 & 1),
+        // so lane r16 receives dim 16 dt + r16 of those 8 tokens, and keeps the
+        // four (4 grp .. 4 grp + 3) its MFMA operand holds.  Codes convert
+        // without scale; each token's scale of the tile's 128-dim group
+        // multiplies its P^T entry instead (powers of two: exact).
+        const LDS_AS char* vbase = reg + (8 * (grp >> 1) + (r16 >> 1)) * kF8RowBytes + 8 * (r16 & 1);
+        s16x4_t pg[4];
+        {
+          f32x4_t tsc[4];  // scales of tokens 4 grp + i, all four groups
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tsc[i] = *(const LDS_AS f32x4_t*)(reg + (4 * grp + i) * kF8RowBytes + kLatent);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const u32x2_t v = {pack_bf16(pr[0] * tsc[0][g], pr[1] * tsc[1][g]), pack_bf16(pr[2] * tsc[2][g], pr[3] * tsc[3][g])};
+            pg[g] = __builtin_bit_cast(s16x4_t, v);
+          }
+        }
+        constexpr int kVAhead = 8;
+        i32x2_t vr[kVAhead + 1];
+#pragma unroll
+        for (int i = 0; i < kVAhead; ++i)
+          vr[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(vbase + 16 * i));
+        __builtin_amdgcn_sched_group_barrier(0x100, kVAhead, 0);
+#pragma unroll
+        for (int dt = 0; dt < 32; ++dt) {
+          if (dt + kVAhead < 32) {
+            const int n = dt + kVAhead;
+            vr[n % (kVAhead + 1)] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(vbase + 16 * n));
+          }
+          const i32x2_t c = vr[dt % (kVAhead + 1)];
+          const unsigned word = (unsigned)((grp & 1) ? c[1] : c[0]);
+          const u32x2_t vb = {cvt_fp8x2(word, 1.0f, false), cvt_fp8x2(word, 1.0f, true)};
+          O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, vb), pg[dt >> 3], O[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100 | 0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      } else {
         constexpr int kVAhead = 8;
         bf16x4_t va[kVAhead + 1];
 #pragma unroll
@@ -403,7 +457,7 @@ decode_tokensplit(DecodeParams p) {
     // ---- merge the four waves' partial softmax states through LDS (the
     // buffer just consumed, buf ^ 1, of every wave), then write
     // the merge goes through a region no transfer targets: the slot just
-    // consumed (bf16) or the dequantised slice (FP8)
+    // consumed (bf16) or the merge region (FP8)
     const int dbuf = kFp8 ? 2 * kF8SliceBytes : (buf ^ 1) * kSliceBytes;
     wg_barrier();  // every wave is done with its slices
     if (lane < 16) *(LDS_AS f32x2_t*)(mstat + (w * 16 + lane) * 2) = f32x2_t{m_run, l_run};
@@ -579,24 +633,6 @@ __device__ __forceinline__ PageDmaF8 fp8_page_dma_offsets(int w, int kvh, int h_
 __device__ __forceinline__ void dma_piece_f8(LDS_AS char* page, i32x4_t rsrc, const PageDmaF8& d, int w, int i) {
   if (w + 4 * i < kF8PageDma) dma16(page + 1024 * (w + 4 * i), rsrc, d.off[i]);
 }
-// 8 e4m3 codes (two words) -> 8 bf16 times a power-of-two scale (exact)
-__device__ __forceinline__ bf16x8_t cvt8_fp8(unsigned w0, unsigned w1, float sc) {
-  const u32x4_t r = {cvt_fp8x2(w0, sc, false), cvt_fp8x2(w0, sc, true), cvt_fp8x2(w1, sc, false),
-                     cvt_fp8x2(w1, sc, true)};
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-// 8 bf16 values, element j times sc[j] (powers of two: exact while the
-// products stay in bf16's normal range)
-__device__ __forceinline__ bf16x8_t scale8(bf16x8_t v, const float* sc) {
-  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = pack_bf16(__builtin_bit_cast(float, u[i] << 16) * sc[2 * i],
-                     __builtin_bit_cast(float, u[i] & 0xffff0000u) * sc[2 * i + 1]);
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 template <bool kSparse, bool kFp8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
