@@ -183,12 +183,12 @@ int oracle_decode(const uint16_t* q, const uint16_t* kcache, long long num_pages
  * j the last sequence whose work starts before hi, last = min(hi, B_j) - 1;
  * an empty part (lo >= T) is {b, 0, b, 0, 0, 0, 0, 0}.
  *
- * Tile rows and the constants: rows <= 16 -> 16, rows <= 64 -> 64, else 128
+ * Tile rows and the constants: rows <= 16 -> 16, rows <= 128 -> 64, else 128
  * (the row tile one workgroup owns); OVH = 3 for the 16-row tile, tile / 16
  * otherwise; QMIN = 2 * OVH.
  * Written with plain loops over all sequences for every part.
  */
-static int twin_tile_rows(int rows) { return rows <= 16 ? 16 : rows <= 64 ? 64 : 128; }
+static int twin_tile_rows(int rows) { return rows <= 16 ? 16 : rows <= 128 ? 64 : 128; }
 
 int oracle_tile_rows(int rows) { return twin_tile_rows(rows); }
 

@@ -55,8 +55,8 @@ def plan(lib, batch, rows, h_kv, dv=512, cus=256):
 def test_plan(lib):
     rc, P, ws = plan(lib, 64, 16, 1)
     assert rc == MLA_OK and P == 256 and ws == (64 + 256) * 16 * 513 * 4
-    rc, P, ws = plan(lib, 128, 128, 1)  # one 128-row tile per part
-    assert rc == MLA_OK and P == 256 and ws == (128 + 256) * 128 * 513 * 4
+    rc, P, ws = plan(lib, 128, 128, 1)  # two 64-row tiles per part, parts a multiple of 8
+    assert rc == MLA_OK and P == 128 and ws == (128 + 128) * 128 * 513 * 4
     rc, P, _ = plan(lib, 132, 256, 1)  # two 128-row tiles per part, parts a multiple of 8
     assert rc == MLA_OK and P == 128
     rc, P, _ = plan(lib, 8, 64, 1)
@@ -64,7 +64,7 @@ def test_plan(lib):
     rc, P, _ = plan(lib, 1, 16, 3, cus=2)
     assert rc == MLA_OK and P == 1
     assert lib.mla_tile_rows(16) == 16 and lib.mla_tile_rows(17) == 64 and lib.mla_tile_rows(64) == 64
-    assert lib.mla_tile_rows(65) == 128 and lib.mla_tile_rows(256) == 128
+    assert lib.mla_tile_rows(128) == 64 and lib.mla_tile_rows(129) == 128 and lib.mla_tile_rows(256) == 128
 
 
 @pytest.mark.parametrize("args,code", [

@@ -186,6 +186,11 @@ EDGE = [
     ([5000], 1, 64, 1, False, 64),                     # many splits of one sequence
     ([5000], 1, 16, 1, False, 64),
     ([2, 3000, 1, 640], 1, 1, 1, False, None),         # a single query row
+    # more than 128 rows per KV head: 128-row tiles, the last one ragged
+    ([700, 900, 33], 3, 64, 1, True, 9),               # 192 rows
+    ([1200, 5], 2, 100, 1, True, None),                # 200 rows
+    ([4100], 1, 129, 1, False, 32),                    # 129 rows: a one-row second tile, many splits
+    ([300, 2000], 5, 64, 2, True, 6),                  # two KV heads of 160 rows
 ]
 
 

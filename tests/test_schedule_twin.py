@@ -86,7 +86,7 @@ def test_edge_invariants(oracle_lib, seqlens, rows, P):
 def test_chunk_count_closed_form(oracle_lib):
     """chunks_i = part(B_i - 1) - part(A_i) + 1, recomputed from the partition line."""
     seqlens = [218, 1, 0, 5000, 64, 65, 4096]
-    for rows, ovh in [(1, 3), (16, 3), (17, 4), (32, 4), (64, 4), (65, 8), (128, 8), (256, 8)]:
+    for rows, ovh in [(1, 3), (16, 3), (17, 4), (32, 4), (64, 4), (65, 4), (128, 4), (129, 8), (256, 8)]:
         for P in (3, 16, 256):
             md, ns = oracle_lib.schedule(seqlens, rows, P)
             c, A, B = 0, [], []
