@@ -26,7 +26,9 @@
 //     of three: half page h + 3 is requested during step h, two steps ahead of
 //     its use, in the slots half pages h - 1 (latent) and h (rope) just left;
 //   * V^T is read from the latent slot with the transposed LDS read
-//     (ds_read_b64_tr_b16); each V element is read once per 128 rows.
+//     (ds_read_b64_tr_b16); each V element is read once per 128 rows;
+//   * at a chunk's end each wave's O goes through LDS (the latent slots are
+//     free then) so that every store writes whole 512-byte row segments.
 // Page transfers, the slice swizzle, the lazy rescale (the running max moves
 // only when it grows by more than 2^8) and the chunk bookkeeping are those of
 // decode.hip (decode_common.h).
@@ -46,7 +48,9 @@ constexpr int kWPbuf = kWRope + 3 * kRopeSlot;     // 2 x P [128 rows][32 tokens
 constexpr int kWPBytes = kWRows * kHalf * 2;
 constexpr int kWAbuf = kWPbuf + 2 * kWPBytes;      // 2 x alpha [128] fp32
 constexpr int kWLbuf = kWAbuf + 2 * kWRows * 4;    // 1 / l [128] fp32 at the chunk end
-constexpr int kWLds = kWLbuf + kWRows * 4;
+constexpr int kWRbuf = kWLbuf + kWRows * 4;        // output row offsets [128] int at the chunk end
+constexpr int kWLds = kWRbuf + kWRows * 4;
+constexpr int kWStage = 32 * 1024;                 // per wave: 64 rows x 128 dims fp32 of O (in the latent slots)
 constexpr int kWDma = 9;                           // transfers per wave per half page
 static_assert(kWLds <= 160 * 1024, "LDS budget");
 
@@ -56,6 +60,7 @@ decode_wide(DecodeParams p) {
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
   LDS_AS float* lbuf = (LDS_AS float*)(smem + kWLbuf);
+  LDS_AS int* rbuf = (LDS_AS int*)(smem + kWRbuf);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -134,6 +139,7 @@ decode_wide(DecodeParams p) {
     }
     int ids = load_page_ids(p, b, sr.lo, lane);
     vm_drain();
+    wg_barrier();  // every wave is done with the previous chunk's output staging in the slots
 
     // half page h lives in latent slot (h - h0) & 3 and rope slot (h - h0) % 3;
     // transfer g < 8 of a wave moves latent chunk group g, transfer 8 the rope group
@@ -146,9 +152,8 @@ decode_wide(DecodeParams p) {
       if (g < 8) dma16(smem + kWLat + lat * kLatSlot + dma_lat + g * kGroupBytes, r, vb);
       else dma16(smem + kWRope + rope * kRopeSlot + dma_rope, r, vb);
     };
-    auto nothing = [](int) {};
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < 2; ++k) {
       const i32x4_t r = h0 + k < h1 ? half_rsrc(h0 + k) : make_rsrc(p.kcache, 0u);
 #pragma unroll
       for (int g = 0; g < kWDma; ++g) dma_piece_h(h0 + k, r, k, k, g);
@@ -296,10 +301,14 @@ decode_wide(DecodeParams p) {
     };
 
     if (h0 < h1) {
-      wait_vmcnt<2 * kWDma>();
+      wait_vmcnt<kWDma>();
       wg_barrier();  // half page h0 visible
       f32x16_t S;
-      qk(kWLat, kWRope, S, nothing);
+      // half page h0 + 2's transfers, one per four MFMAs of QK^T(h0)
+      const i32x4_t r2 = h0 + 2 < h1 ? half_rsrc(h0 + 2) : make_rsrc(p.kcache, 0u);
+      qk(kWLat, kWRope, S, [&](int ks) {
+        if ((ks & 3) == 0) dma_piece_h(h0 + 2, r2, 2, 2, ks >> 2);
+      });
 #pragma unroll
       for (int st = 0; st < kSoftSteps; ++st) soft_step(h0, S, st, true);
     }
@@ -346,44 +355,83 @@ decode_wide(DecodeParams p) {
       rope = rope1;
     }
 
-    // ---- chunk end: the row owner publishes 1 / l and writes lse; every wave
-    // normalises and stores its 128 output dims of all 128 rows
+    // ---- chunk end: the row owner publishes 1 / l and its row's output offset
+    // and writes lse; every wave normalises its 128 output dims of all 128 rows
+    // and stores them through its own 32 KB of the latent slots, 64 rows at a
+    // time, so that each store writes two whole 512-byte row segments rather
+    // than 32-byte pieces of 32 rows
     const bool split = sr.chunks > 1;
     const long long slot_base = ((long long)(sr.base + sr.ord) * p.h_kv + kvh) * p.rows;
     if (hb == 0) {
       lbuf[trow] = l_run > 0.f ? 1.f / l_run : 0.f;
+      rbuf[trow] = (qrow_ok && sr.ok) ? (int)(split ? slot_base + qrow : qo) : -1;
       if (qrow_ok && sr.ok) {
         const float l2 = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : -INFINITY;
         if (split) p.lse_acc[slot_base + qrow] = l2;
         else p.lse[qo] = l2 * kLn2;
       }
     }
-    wg_barrier();  // 1 / l of every row visible; every wave is done with the slots
+    // transfers past the chunk's end (empty ranges) write the slots: they land
+    // before the slots hold output
+    wait_vmcnt<0>();
+    wg_barrier();  // 1 / l and offsets of every row visible; every wave is done with the slots
+    // Lane base offsets, recomputed per chunk (kept out of loop-invariant
+    // hoisting, which would hold one register per address across the page
+    // loop); everything else is an immediate offset.  Staging row R = 32 r2 +
+    // l32 holds tile row 64 half + R; its 16-byte chunk c (dims 4c .. 4c + 3 of
+    // the wave's 128) sits at position c ^ (R & 7): the 8 rows (or 8 chunks)
+    // one LDS pass serves fall on distinct banks.
+    int wb[4], rb[4], ob = kWRbuf + 4 * hb;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int orow = mt * kWRows + 32 * rt + l32;
-      const float inv = lbuf[32 * rt + l32];
-      if (orow < p.rows && sr.ok) {
-        int os;
-        long long oo;
-        row_coords(p, b, kvh, orow, os, oo);
-        const long long off = (split ? slot_base + orow : oo) * kDv + 128 * w + 4 * hb;
+    for (int j = 0; j < 4; ++j) {
+      wb[j] = kWLat + w * kWStage + l32 * 512 + (((2 * j + hb) ^ (l32 & 7)) << 4);
+      rb[j] = kWLat + w * kWStage + hb * 512 + ((l32 ^ ((2 * j + hb) & 7)) << 4);
+      asm volatile("" : "+v"(wb[j]), "+v"(rb[j]));
+    }
+    asm volatile("" : "+v"(ob));
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int r2 = 0; r2 < 2; ++r2) {
+        const int rt = 2 * half + r2;
+        const float inv = lbuf[32 * rt + l32];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const f32x16_t o = acc_out(O[dt][rt]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4_t v = {o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
-            const long long d = off + 32 * dt + 8 * j;
-            if (split) {
-              *(f32x4_t*)(p.o_acc + d) = v;
-            } else {
-              const u32x2_t pk = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
-              *(u32x2_t*)(p.out + d) = pk;
+          for (int j = 0; j < 4; ++j)  // chunk 8 dt + 2 j + hb
+            *(LDS_AS f32x4_t*)(smem + wb[j] + r2 * 32 * 512 + dt * 128) =
+                f32x4_t{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
+        }
+      }
+      // lanes 0-31 store staging row 2k, lanes 32-63 row 2k + 1: chunk l32
+      // each; eight rows' data and offsets are read before their stores
+      auto store_half = [&](auto split_tag) {
+#pragma unroll
+        for (int k0 = 0; k0 < 32; k0 += 8) {
+          f32x4_t v[8];
+          int ro[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            v[i] = *(const LDS_AS f32x4_t*)(smem + rb[(k0 + i) & 3] + (k0 + i) * 1024);
+            ro[i] = *(const LDS_AS int*)(smem + ob + 4 * (64 * half + 2 * (k0 + i)));
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (ro[i] >= 0) {
+              const long long d = (long long)ro[i] * kDv + 128 * w + 4 * l32;
+              if constexpr (decltype(split_tag)::value) {
+                *(f32x4_t*)(p.o_acc + d) = v[i];
+              } else {
+                const u32x2_t pk = {pack_bf16(v[i][0], v[i][1]), pack_bf16(v[i][2], v[i][3])};
+                *(u32x2_t*)(p.out + d) = pk;
+              }
             }
           }
         }
-      }
+      };
+      if (split) store_half(std::true_type{});
+      else store_half(std::false_type{});
     }
   }
   // transfers past the last chunk's end (empty ranges) may still be in flight:
