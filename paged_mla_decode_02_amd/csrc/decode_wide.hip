@@ -195,55 +195,62 @@ decode_wide(DecodeParams p) {
 
     // online softmax of half page h from its scores S (raw dot products): lane
     // holds row trow, tokens 8 (r >> 2) + 4 hb + (r & 3) of the half page.
-    // Written as kSoftSteps pieces of a few VALU instructions each so that
-    // they interleave with the MFMAs of PV: the masked maximum in two halves,
-    // one exponential per piece, then the bf16 packing and P writes.
-    constexpr int kSoftSteps = 23;
+    // Written as kSoftSteps pieces placed one after each MFMA of PV.  A wave
+    // issues about 16 cycles of VALU work under a 32-cycle MFMA, so each piece
+    // stays near that: the masked maximum in two halves, then one scaling FMA
+    // and the previous element's exponential (a quarter-rate instruction) per
+    // piece, then the sums and bf16 packing two elements at a time.
+    constexpr int kSoftSteps = 30;
     float sx[16];
     float alpha = 1.f, m_use = 0.f, psum = 0.f, mx = -INFINITY;
+    unsigned pk0 = 0u;
     bool partial = false;
     // With live == false (no half page h: the chunk's last PV step) the
     // pieces still run, on zero scores, so the PV loop has no per-element
     // selects; they then write only P and alpha slots that nothing reads and
     // leave the running maximum and sum alone.
     auto soft_step = [&](int h, const f32x16_t& S, int st, bool live) {
-      if (st <= 1) {
-        if (st == 0) {
-          // only a half page that reaches past a row's last visible key is
-          // masked (a wave-uniform branch: whole half pages skip it)
-          partial = __builtin_amdgcn_ballot_w64((h + 1) * kHalf > nkeys) != 0;
-          mx = -INFINITY;
-        }
+      if (st == 0) {
+        // only a half page that reaches past a row's last visible key is
+        // masked (a wave-uniform branch: whole half pages skip it)
+        partial = __builtin_amdgcn_ballot_w64((h + 1) * kHalf > nkeys) != 0;
 #pragma unroll
-        for (int r = 8 * st; r < 8 * st + 8; ++r) sx[r] = S[r];
+        for (int r = 0; r < 16; ++r) sx[r] = S[r];
         if (__builtin_expect(partial, 0)) {
           const int lim = nkeys - h * kHalf - 4 * hb;  // visible tokens from this lane's first position
 #pragma unroll
-          for (int r = 8 * st; r < 8 * st + 8; ++r)
+          for (int r = 0; r < 16; ++r)
             if (8 * (r >> 2) + (r & 3) >= lim) sx[r] = -INFINITY;
         }
+      } else if (st <= 2) {
+        if (st == 1) mx = -INFINITY;
 #pragma unroll
-        for (int r = 8 * st; r < 8 * st + 8; ++r) mx = fmaxf(mx, sx[r]);
-        if (st == 1) {
-          const float m = half_max(mx) * p.scale_log2;
-          alpha = 1.f;
-          if (live && m > m_run + kTau) {  // the reference moves (at the first visible key O and l are 0: alpha stays 1)
-            if (m_run != -INFINITY) alpha = __builtin_amdgcn_exp2f(m_run - m);
-            m_run = m;
-            l_run *= alpha;
-          }
-          m_use = (m_run == -INFINITY) ? 0.f : m_run;
-          psum = 0.f;
+        for (int r = 8 * (st - 1); r < 8 * st; ++r) mx = fmaxf(mx, sx[r]);
+      } else if (st == 3) {
+        const float m = half_max(mx) * p.scale_log2;
+        alpha = 1.f;
+        if (live && m > m_run + kTau) {  // the reference moves (at the first visible key O and l are 0: alpha stays 1)
+          if (m_run != -INFINITY) alpha = __builtin_amdgcn_exp2f(m_run - m);
+          m_run = m;
+          l_run *= alpha;
         }
-      } else if (st <= 17) {
-        const int r = st - 2;
-        sx[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], p.scale_log2, -m_use));
-        psum += sx[r];
-      } else if (st <= 21) {
-        const int j = st - 18;
-        const int pw = kWPbuf + (h & 1) * kWPBytes + pwx;
-        const u32x2_t v = {pack_bf16(sx[4 * j], sx[4 * j + 1]), pack_bf16(sx[4 * j + 2], sx[4 * j + 3])};
-        *(LDS_AS u32x2_t*)(smem + (pw ^ (j << 4))) = v;
+        m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        psum = 0.f;
+      } else if (st <= 20) {
+        const int j = st - 4;
+        if (j < 16) sx[j] = __builtin_fmaf(sx[j], p.scale_log2, -m_use);
+        if (j >= 1) sx[j - 1] = __builtin_amdgcn_exp2f(sx[j - 1]);
+      } else if (st <= 28) {
+        const int q = st - 21;
+        psum += sx[2 * q];
+        psum += sx[2 * q + 1];
+        const unsigned pk = pack_bf16(sx[2 * q], sx[2 * q + 1]);
+        if (q & 1) {
+          const int pw = kWPbuf + (h & 1) * kWPBytes + pwx;
+          *(LDS_AS u32x2_t*)(smem + (pw ^ ((q >> 1) << 4))) = u32x2_t{pk0, pk};
+        } else {
+          pk0 = pk;
+        }
       } else {
         const float ps = half_sum(psum);
         if (live) l_run += ps;
