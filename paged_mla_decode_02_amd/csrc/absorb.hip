@@ -31,7 +31,6 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;                 // tokens per MFMA tile, columns per MFMA tile
-constexpr int kCols = 128;                // absorb: output columns per workgroup
 constexpr int kChunk = 4 * kTile;         // absorb: tokens per workgroup (one tile per wave)
 constexpr int kWtStride = kNope + 8;      // LDS row (one output column) of the transposed W_UK slice, padded
 constexpr int kObStride = kLatent + 8;    // LDS row (one token) of the staged o_lat tile, padded
@@ -67,10 +66,13 @@ __device__ __forceinline__ void store_tile(uint16_t* stage, uint16_t* out, long 
 }
 
 // Grid (h_q, kLatent / kCols, ceil(tokens / kChunk)); 4 waves.  The workgroup
-// owns 128 output columns of one head and kChunk tokens: the transposed
-// 128 x 128 W_UK slice sits in LDS and every wave applies all of it (4 column
-// tiles) to its own 32-token tile, so each q_nope row is read once per column
-// group and each weight slice once per token chunk.
+// owns kCols output columns of one head and kChunk tokens: the transposed
+// 128 x kCols W_UK slice sits in LDS and every wave applies all of it to its
+// own 32-token tile, so each q_nope row is read once per column group and each
+// weight slice once per token chunk.  kCols = 128 (4 column tiles per wave)
+// when there are workgroups enough to fill the GPU, else 32: four times the
+// workgroups, each with a quarter of the weight slice to bring in.
+template <int kCols>
 __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __restrict__ q_nope,
                                                             const uint16_t* __restrict__ q_rope,
                                                             const uint16_t* __restrict__ w_uk, int tokens, int h_q,
@@ -126,6 +128,50 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(const uint16_t* __re
   }
 }
 
+// Grid (h_q, kDvOut / kTile, ceil(tokens / kTile)); 4 waves; for few tokens,
+// when the kernel below would leave most of the GPU idle.  The workgroup owns
+// one 32-column x 32-token output tile of one head; wave w sums latent indices
+// 128 w .. 128 w + 127 (its W_UV block and o_lat block go straight to
+// registers), and the four partial tiles are added through LDS.
+__global__ __launch_bounds__(kThreads) void unabsorb_out_split_kernel(const uint16_t* __restrict__ o_lat,
+                                                                      const uint16_t* __restrict__ w_uv,
+                                                                      int tokens, int h_q,
+                                                                      uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) float part[3][16][64];  // waves 1..3: [wave - 1][element][lane]
+  __shared__ __attribute__((aligned(16))) uint16_t stage[kTile * kOutStride];
+  const int h = blockIdx.x;
+  const int c0 = blockIdx.y * kTile;
+  const int t0 = blockIdx.z * kTile;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int t = t0 + (lane & 31);
+  const int kb = kLatent / 4 * w + 8 * (lane >> 5);
+  // A operand: row c0 + (lane & 31) of W_UV[h]; B operand: token t (token 0's
+  // row past the last token, never stored); latent indices kb + 16 ks .. +7
+  const bf16x8_t* asrc = (const bf16x8_t*)(w_uv + ((long long)h * kDvOut + c0 + (lane & 31)) * kLatent + kb);
+  const bf16x8_t* bsrc = (const bf16x8_t*)(o_lat + ((long long)(t < tokens ? t : 0) * h_q + h) * kLatent + kb);
+  constexpr int kSteps = kLatent / 4 / 16;
+  bf16x8_t a[kSteps], b[kSteps];
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) {
+    a[ks] = asrc[2 * ks];
+    b[ks] = bsrc[2 * ks];
+  }
+  f32x16_t acc = {};
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], b[ks], acc, 0, 0, 0);
+  if (w > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[w - 1][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += part[0][r][lane] + part[1][r][lane] + part[2][r][lane];
+    store_tile(stage, out + (long long)h * kDvOut + c0, (long long)h_q * kDvOut, tokens, t0, acc, lane);
+  }
+}
+
 // Grid (h_q, ceil(tokens / kTile)); 4 waves.  The workgroup owns all 128
 // output columns of one head (wave w: columns 32 w .. +31, its W_UV rows held
 // in registers) for one 32-token tile, whose o_lat rows are staged once in LDS.
@@ -167,17 +213,34 @@ __global__ __launch_bounds__(kThreads) void unabsorb_out_kernel(const uint16_t* 
 
 }  // namespace
 
+// The narrow forms are chosen when the wide ones would launch fewer
+// workgroups than twice (absorb) or once (unabsorb) the GPU's 256 CUs.
+static bool absorb_narrow(int tokens, int h_q) {
+  return h_q * (kLatent / 128) * ((tokens + kChunk - 1) / kChunk) < 512;
+}
+static bool unabsorb_split(int tokens, int h_q) { return h_q * ((tokens + kTile - 1) / kTile) < 256; }
+
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int tokens,
                            int h_q, uint16_t* q_abs, hipStream_t stream) {
-  const dim3 grid(h_q, kLatent / kCols, (tokens + kChunk - 1) / kChunk);
-  hipLaunchKernelGGL(absorb_q_kernel, grid, dim3(kThreads), 0, stream, q_nope, q_rope, w_uk, tokens, h_q, q_abs);
+  const int chunks = (tokens + kChunk - 1) / kChunk;
+  if (absorb_narrow(tokens, h_q))
+    hipLaunchKernelGGL(absorb_q_kernel<32>, dim3(h_q, kLatent / 32, chunks), dim3(kThreads), 0, stream, q_nope,
+                       q_rope, w_uk, tokens, h_q, q_abs);
+  else
+    hipLaunchKernelGGL(absorb_q_kernel<128>, dim3(h_q, kLatent / 128, chunks), dim3(kThreads), 0, stream, q_nope,
+                       q_rope, w_uk, tokens, h_q, q_abs);
   return hipGetLastError();
 }
 
 hipError_t launch_unabsorb_out(const uint16_t* o_lat, const uint16_t* w_uv, int tokens, int h_q, uint16_t* out,
                                hipStream_t stream) {
-  const dim3 grid(h_q, (tokens + kTile - 1) / kTile);
-  hipLaunchKernelGGL(unabsorb_out_kernel, grid, dim3(kThreads), 0, stream, o_lat, w_uv, tokens, h_q, out);
+  const int tiles = (tokens + kTile - 1) / kTile;
+  if (unabsorb_split(tokens, h_q))
+    hipLaunchKernelGGL(unabsorb_out_split_kernel, dim3(h_q, kDvOut / kTile, tiles), dim3(kThreads), 0, stream,
+                       o_lat, w_uv, tokens, h_q, out);
+  else
+    hipLaunchKernelGGL(unabsorb_out_kernel, dim3(h_q, tiles), dim3(kThreads), 0, stream, o_lat, w_uv, tokens, h_q,
+                       out);
   return hipGetLastError();
 }
 
