@@ -73,7 +73,13 @@ def bits_of(torch, t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("batch,s_q,h_q", [(1, 1, 1), (2, 1, 16), (3, 11, 5), (64, 1, 16), (132, 2, 128)])
+# Each GEMM has a form for few tokens and one for many, picked by the grid size:
+# absorb takes 32-column workgroups while h_q * 4 * ceil(T / 128) < 512 and the
+# up-projection splits its reduction over the waves while h_q * ceil(T / 32) <
+# 256.  T = 128, h_q = 64 takes the narrow absorb with the wide up-projection;
+# T = 264, h_q = 128 the wide form of both; the others the narrow forms.
+@pytest.mark.parametrize("batch,s_q,h_q", [(1, 1, 1), (2, 1, 16), (3, 11, 5), (64, 1, 16), (64, 2, 64),
+                                           (132, 2, 128)])
 def test_absorb_and_unabsorb(env, batch, s_q, h_q):
     torch, mla, ml, dev = env
     lay = make_layer_inputs(batch, s_q, h_q, seed=batch * 7 + h_q)
