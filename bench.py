@@ -72,7 +72,7 @@ def algorithmic(w, row_bytes=576 * 2):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("decode.hip", "decode_wide.hip", "decode_common.h", "mla_kernels.h"):
+    for f in ("decode.hip", "decode_wide.hip", "decode_qkpv.hip", "decode_common.h", "mla_kernels.h"):
         with open(os.path.join(ROOT, "paged_mla_decode_02_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

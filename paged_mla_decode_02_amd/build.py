@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libmla.so")
 SYNC_LIB_PATH = os.path.join(HERE, "libmla_sync.so")
-SOURCES = ["api.cpp", "pager.cpp", "sched.hip", "decode.hip", "decode_wide.hip", "combine.hip", "absorb.hip", "kv_append.hip", "sparse.hip",
+SOURCES = ["api.cpp", "pager.cpp", "sched.hip", "decode.hip", "decode_wide.hip", "decode_qkpv.hip", "combine.hip", "absorb.hip", "kv_append.hip", "sparse.hip",
            "noalloc.hip"]
 ARCH = "gfx950"
 

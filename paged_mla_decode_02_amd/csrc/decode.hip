@@ -1099,7 +1099,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   q.xcd_map = (q.m_tiles * q.h_kv > 1 && q.num_parts % 8 == 0) ? 1 : 0;
   if (q.kv_fp8) return launch_one<decode_pairsplit<false, true>>(kPsLds, q, stream);
   if (q.sparse) return launch_one<decode_pairsplit<true, false>>(kPsLds, q, stream);
-  return launch_one<decode_pairsplit<false, false>>(kPsLds, q, stream);
+  return launch_decode_qkpv(q, stream);
 }
 
 }  // namespace mla

@@ -1,0 +1,438 @@
+// Paged MLA decode, 64-row tiles with two kinds of waves: the kernel for 17 to
+// 64 query rows per KV head on bf16 pages, and for each 64-row tile of 65 to
+// 128 rows.  Same method as decode.hip and decode_wide.hip -- every latent page
+// read from HBM is multiplied against all query rows that share its KV head
+// ("OpenSourceWeek Day 1 -- Demystifying DeepSeek's FlashMLA",
+// deepseekonline.chat, §II.1), the softmax is computed online with a running
+// max and sum and equals the textbook result ("FlashMLA inference
+// acceleration" notes, dpshk.com, §2.2) -- with the work of a step split
+// between the waves by kind rather than by rows or dims:
+//
+//   * waves 0 and 1 (score waves) own rows 32w .. 32w+31 of the tile: their
+//     queries stay in 144 VGPRs; in step h they compute the scores of half
+//     page h + 1 (QK^T) and its online softmax, and publish P(h + 1) and the
+//     rows' rescale factors through LDS (both double-buffered);
+//   * waves 2 and 3 (value waves) own output dims 256(w-2) .. +255 of all 64
+//     rows: O^T is 8 x 2 tiles of 32 x 32 fp32, the whole AGPR file, updated
+//     only through the inline-assembly MFMAs of decode_common.h; in step h they
+//     run PV of half page h and issue every page transfer (one 16-token slice
+//     of each half page per wave, spread between the PV MFMAs);
+//   * a step is one barrier plus the longer of the two kinds' work, which run
+//     at the same time on their own SIMDs.  The 128-row kernel cannot split
+//     its waves this way: 128 rows need all four AGPR files for O and all four
+//     VGPR files for the queries;
+//   * the latent part of a half page lives in one of four LDS slots and its
+//     rope part in one of three: in step h the value waves read slot h, the
+//     score waves slot h + 1, half page h + 2 is landing and h + 3 is requested
+//     into the slots half pages h - 1 (latent) and h (rope) left.
+// Page transfers, the slice swizzle and the chunk bookkeeping are those of
+// decode_common.h.  The lazy rescale is that of the other kernels with a
+// larger threshold (below).
+#include "decode_common.h"
+
+namespace mla {
+namespace {
+
+constexpr int kQRows = 64;                          // query rows of the tile
+constexpr int kQHalf = 32;                          // tokens per step
+constexpr int kQLatSlice = 8 * kGroupBytes;         // 16 KB: 16 tokens x 512 latent dims
+constexpr int kQLatSlot = 2 * kQLatSlice;           // 32 KB per half page
+constexpr int kQRopeSlot = 2 * kGroupBytes;         // 4 KB per half page (2 x 16 tokens x 64 dims)
+constexpr int kQLat = 0;                            // 4 latent slots
+constexpr int kQRope = kQLat + 4 * kQLatSlot;       // 3 rope slots
+constexpr int kQPbuf = kQRope + 3 * kQRopeSlot;     // 2 x P [64 rows][32 tokens] bf16
+constexpr int kQPBytes = kQRows * kQHalf * 2;
+constexpr int kQAbuf = kQPbuf + 2 * kQPBytes;       // 2 x alpha [64] fp32
+constexpr int kQLbuf = kQAbuf + 2 * kQRows * 4;     // 1 / l [64] fp32 at the chunk end
+constexpr int kQRbuf = kQLbuf + kQRows * 4;         // output row offsets [64] int at the chunk end
+constexpr int kQLds = kQRbuf + kQRows * 4;
+constexpr int kQStage = 2 * kQLatSlot;              // per value wave: 64 rows x 256 dims fp32 of O
+constexpr int kQDma = 2 * (kLatent / 64 + 1);       // transfers per value wave per half page (18)
+static_assert(kQLds <= 160 * 1024, "LDS budget");
+// Lazy-rescale threshold, log2 units: the running max moves only when a half
+// page's maximum exceeds it by more than 2^64.  Rescaling O costs a value wave
+// ~770 VALU instructions on its 256 AGPRs, on the step's critical path; with
+// 2^8 (the other kernels' threshold) a workload whose keys include 1 % scaled
+// outliers rescaled about a fifth of its steps.  P then stays below 2^64 and
+// the sums below 2^64 times the key count: far inside the bf16 / fp32
+// exponent range (bf16 pages only: no FP8 scale multiplies P here).
+constexpr float kQTau = 64.0f;
+
+// PV MFMA i of a step (0..31) is followed by transfer dma_at(i) of the next
+// half page but two, or by none (-1): the transfers spread evenly.
+__host__ __device__ constexpr int dma_at(int i) {
+  for (int g = 0; g < kQDma; ++g)
+    if ((32 * g) / kQDma == i) return g;
+  return -1;
+}
+
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+decode_qkpv(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
+  LDS_AS char* smem = (LDS_AS char*)smem_generic;
+  LDS_AS float* lbuf = (LDS_AS float*)(smem + kQLbuf);
+  LDS_AS int* rbuf = (LDS_AS int*)(smem + kQRbuf);
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scorer = w < 2;
+  const int wk = w & 1;  // index among the waves of its kind
+  int part, mt, kvh;
+  map_block(p, part, mt, kvh);
+  const int32_t* md = p.tile_md + (long long)part * kMdInts;
+  const int i0 = md[0], f0 = md[1], e0 = md[3], ord0 = md[4];
+  const int j0 = min(md[2], p.batch - 1);
+  if (i0 >= p.batch || i0 < 0) return;
+
+  const int l32 = lane & 31;
+  const int hb = lane >> 5;
+  const int g16 = lane >> 4;
+  const int k16 = lane & 15;
+  const int trow = 32 * wk + l32;  // score waves: tile row of this lane
+  const int qrow = mt * kQRows + trow;
+  const bool qrow_ok = qrow < p.rows;
+
+  // K operand of QK^T (score waves): token l32 of the half page, 8 dims per
+  // k-step, addressed as in the 128-row kernel ((base ^ ((ks & 3) << 5)) +
+  // (ks / 4) groups; latent k-steps 0..31, rope k-steps 32..35)
+  const int kx = slice_off(l32 & 15, hb);
+  const int klat = (l32 >> 4) * kQLatSlice + kx;
+  const int krope = (l32 >> 4) * kGroupBytes + kx;
+  // V^T operand of PV (value waves, transposed read): k-step ks is slice ks,
+  // tokens 8 (g16 >> 1) + k16 / 4 (+4 p4); dims 256 wk + 32 dt + 16 (g16 & 1) +
+  // 4 (k16 & 3): chunk group 4 wk + dt / 2, the odd dim tile flipping address
+  // bit 6
+  int vx;
+  {
+    const int t = 8 * (g16 >> 1) + (k16 >> 2);
+    const int pos = 2 * (g16 & 1) + ((k16 & 3) >> 1);
+    vx = t * 128 + ((pos ^ swz(t)) << 4) + ((k16 & 1) << 3) + 4 * wk * kGroupBytes;
+  }
+  // P^T operand of PV: row 32 rt + l32, tokens 16 ks + 8 hb .. +7: px ^ (ks << 5)
+  const int px = wp_off(l32, hb);
+  // P write of the softmax: row trow, tokens 8 j + 4 hb .. +3: (buffer + pwx) ^ (j << 4)
+  const int pwx = wp_off(trow, 0) + 8 * hb;
+
+  // transfers (value waves): slice wk of each half page, i.e. tokens 16 wk ..
+  // 16 wk + 15 of the first (d0) or second (d1) half of a page
+  const SliceDma d0 = slice_dma_offsets(kSlice * wk, kvh, p.h_kv, lane);
+  const SliceDma d1 = slice_dma_offsets(kQHalf + kSlice * wk, kvh, p.h_kv, lane);
+
+  for (int b = i0; b <= j0; ++b) {
+    const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
+    int s;
+    long long qo;
+    row_coords(p, b, kvh, qrow_ok ? qrow : 0, s, qo);
+    const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
+    const int h0 = 2 * sr.lo;
+    const int h1 = min(2 * sr.hi, (sr.L + kQHalf - 1) / kQHalf);
+
+    // One page loop per kind of wave (the same barriers, step for step), so
+    // that the score waves' queries and the value waves' O are never live in
+    // the same code.
+    int ids = load_page_ids(p, b, sr.lo, lane);
+    auto half_rsrc = [&](int h) {
+      const int blk = h >> 1;
+      return page_rsrc(p, page_id(ids, (blk - sr.lo) & 63), blk, sr.L);
+    };
+    // transfer i (0..17) of half page h by a value wave: chunk group i / 2
+    // (group 8 is the rope part), token half i % 2
+    auto dma_piece_h = [&](int h, i32x4_t r, int lat, int rope, int i) {
+      const int g = i >> 1, th = i & 1;
+      const int vb = ((h & 1) ? (th ? d1.vbase[1] : d1.vbase[0]) : (th ? d0.vbase[1] : d0.vbase[0])) + g * 128;
+      if (g < 8) dma16(smem + kQLat + lat * kQLatSlot + wk * kQLatSlice + g * kGroupBytes + th * 1024, r, vb);
+      else dma16(smem + kQRope + rope * kQRopeSlot + wk * kGroupBytes + th * 1024, r, vb);
+    };
+    auto prologue_dma = [&]() {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const i32x4_t r = h0 + k < h1 ? half_rsrc(h0 + k) : make_rsrc(p.kcache, 0u);
+#pragma unroll
+        for (int g = 0; g < kQDma; ++g) dma_piece_h(h0 + k, r, k, k, g);
+      }
+    };
+    // the resource of half page hd's transfers: past the chunk's end an empty
+    // buffer range (it reads zeros and touches no memory, so every step has the
+    // same transfers in flight)
+    auto step_rsrc = [&](int hd) {
+      i32x4_t dr = make_rsrc(p.kcache, 0u);
+      if (hd < h1) {
+        if ((((hd >> 1) - sr.lo) & 63) == 0 && (hd & 1) == 0) {
+          // the next 64 pages' ids (once per 64 pages); drained here, so the
+          // compiler needs no wait for them that would also wait for the page
+          // transfers in flight
+          ids = load_page_ids(p, b, hd >> 1, lane);
+          vm_drain();
+        }
+        dr = half_rsrc(hd);
+      }
+      return dr;
+    };
+    const bool split = sr.chunks > 1;
+    const long long slot_base = ((long long)(sr.base + sr.ord) * p.h_kv + kvh) * p.rows;
+    // Step h, for h = h0 - 1 .. h1 - 1: the score waves score and softmax half
+    // page h + 1; the value waves run PV of half page h (at h0 - 1: P = 0 and
+    // alpha = 1 against half page h0's slot, so that no branch surrounds the PV
+    // assembly) and request half page h + 3 (past the chunk's end with an empty
+    // buffer range: it reads zeros and touches no memory, so every step has the
+    // same transfers in flight).  One barrier per step: half page h + 1 (for
+    // the score waves) and P(h), alpha(h) (for the value waves) become visible
+    // at it, and every wave is done with step h - 1.  Slots of half page h:
+    // latent (h - h0) & 3, rope (h - h0) % 3, counted from h0 - 1.
+    if (scorer) {
+      // queries (B operand, k-step ks = dims 16 ks + 8 hb .. +7), drained
+      // with the page ids before any transfer.  Rows past the last one compute
+      // on row 0's query and are never stored.
+      bf16x8_t qreg[36];
+      {
+        const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) qreg[ks] = qp[2 * ks + hb];
+      }
+      vm_drain();
+      wg_barrier();  // every wave is done with the previous chunk's output staging in the slots
+      float m_run = -INFINITY, l_run = 0.f;  // of row trow (lanes l and l ^ 32 agree)
+      // S^T [32 tokens x 32 rows] of one half page (score waves)
+      auto qk = [&](int lat_off, int rope_off, f32x16_t& S) {
+        constexpr int kAhead = 4;  // K operands in flight ahead of their MFMA
+        bf16x8_t ka[kAhead + 1];
+        const int lb = lat_off + klat, rb = rope_off + krope;
+        auto kread = [&](int n) {
+          const int a = n < 32 ? (lb ^ ((n & 3) << 5)) + (n >> 2) * kGroupBytes : rb ^ ((n & 3) << 5);
+          return *(const LDS_AS bf16x8_t*)(smem + a);
+        };
+        S = f32x16_t{};
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) ka[i] = kread(i);
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+          if (ks + kAhead < 36) ka[(ks + kAhead) % (kAhead + 1)] = kread(ks + kAhead);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S, 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+
+      // online softmax of half page h from its scores S (score waves): lane
+      // holds row trow, tokens 8 (r >> 2) + 4 hb + (r & 3) of the half page.
+      // The same steps as the 128-row kernel's (masked maximum, rescale
+      // decision, exponentials, sums and bf16 packing), run back to back.
+      auto softmax = [&](int h, const f32x16_t& S) {
+        // only a half page that reaches past a row's last visible key is masked
+        // (a wave-uniform branch: whole half pages skip it)
+        const bool partial = __builtin_amdgcn_ballot_w64((h + 1) * kQHalf > nkeys) != 0;
+        float sx[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sx[r] = S[r];
+        if (__builtin_expect(partial, 0)) {
+          const int lim = nkeys - h * kQHalf - 4 * hb;  // visible tokens from this lane's first position
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) >= lim) sx[r] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sx[r]);
+        const float m = half_max(mx) * p.scale_log2;
+        float alpha = 1.f;
+        if (m > m_run + kQTau) {  // the reference moves (at the first visible key O and l are 0: alpha stays 1)
+          if (m_run != -INFINITY) alpha = __builtin_amdgcn_exp2f(m_run - m);
+          m_run = m;
+          l_run *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sx[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], p.scale_log2, -m_use));
+          psum += sx[r];
+        }
+        const int pw = kQPbuf + (h & 1) * kQPBytes + pwx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x2_t v = {pack_bf16(sx[4 * j], sx[4 * j + 1]), pack_bf16(sx[4 * j + 2], sx[4 * j + 3])};
+          *(LDS_AS u32x2_t*)(smem + (pw ^ (j << 4))) = v;
+        }
+        l_run += half_sum(psum);
+        if (hb == 0) ((LDS_AS float*)(smem + kQAbuf + (h & 1) * kQRows * 4))[trow] = alpha;
+      };
+
+      if (h0 < h1) {
+        const int pw = kQPbuf + ((h0 - 1) & 1) * kQPBytes + pwx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(LDS_AS u32x2_t*)(smem + (pw ^ (j << 4))) = u32x2_t{0u, 0u};
+        if (hb == 0) ((LDS_AS float*)(smem + kQAbuf + ((h0 - 1) & 1) * kQRows * 4))[trow] = 1.f;
+      }
+      int lat = 3, rope = 2;
+      for (int h = h0 - 1; h0 < h1 && h < h1; ++h) {
+        const int lat1 = (lat + 1) & 3, rope1 = rope == 2 ? 0 : rope + 1;
+        // half page h + 1 landed (the value waves wait for their transfers before it)
+        wg_barrier();
+        if (h + 1 < h1) {
+          f32x16_t S;
+          qk(kQLat + lat1 * kQLatSlot, kQRope + rope1 * kQRopeSlot, S);
+          softmax(h + 1, S);
+        }
+        lat = lat1;
+        rope = rope1;
+      }
+      // chunk end: publish 1 / l and the row's output offset, write lse
+      if (hb == 0) {
+        lbuf[trow] = l_run > 0.f ? 1.f / l_run : 0.f;
+        rbuf[trow] = (qrow_ok && sr.ok) ? (int)(split ? slot_base + qrow : qo) : -1;
+        if (qrow_ok && sr.ok) {
+          const float l2 = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : -INFINITY;
+          if (split) p.lse_acc[slot_base + qrow] = l2;
+          else p.lse[qo] = l2 * kLn2;
+        }
+      }
+      wg_barrier();  // 1 / l and offsets of every row visible
+    } else {
+      vm_drain();
+      wg_barrier();  // every wave is done with the previous chunk's output staging in the slots
+      prologue_dma();
+      f32x16_t O[8][2];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) acc_zero(O[dt][rt]);
+      // O^T [256 dims x 64 rows] += V^T . P^T over half page h's 32 tokens (value
+      // waves); `between(i)` runs after the i-th of its 32 MFMAs
+      auto pv = [&](int h, int lat_off, auto&& between) {
+        const LDS_AS float* ab = (const LDS_AS float*)(smem + kQAbuf + (h & 1) * kQRows * 4);
+        const float a0 = ab[l32], a1 = ab[32 + l32];
+        const int pb = kQPbuf + (h & 1) * kQPBytes + px;
+        const int vb = lat_off + vx;
+        // column c: k-step c / 8 (slice), dim tile c % 8
+        auto vread = [&](int c) {
+          const int ks = c >> 3, dt = c & 7;
+          const int off = ks * kQLatSlice + (dt >> 1) * kGroupBytes;
+          const bf16x4_t v0 = lds_tr16(smem + (vb ^ ((dt & 1) << 6)) + off);
+          const bf16x4_t v1 = lds_tr16(smem + (vb ^ (16 | ((dt & 1) << 6))) + off + 512);
+          return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8_t bp[2], va[3];
+        va[0] = vread(0);
+        va[1] = vread(1);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) bp[rt] = *(const LDS_AS bf16x8_t*)(smem + pb + rt * 32 * 64);
+        if (__builtin_amdgcn_ballot_w64(a0 != 1.f || a1 != 1.f)) {
+          acc_settle(O[0][0]);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            acc_scale(O[dt][0], a0);
+            acc_scale(O[dt][1], a1);
+          }
+          asm volatile("s_nop 3" ::: "memory");
+        }
+        // the MFMAs are volatile assembly, which LDS reads do not move across:
+        // V^T of column c + 2 is requested after the first MFMA of column c, the
+        // P^T operands of k-step 1 after the last k-step-0 MFMA that reads them
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            pv_mfma(O[c & 7][rt], va[c % 3], bp[rt]);
+            if (rt == 0 && c + 2 < 16) va[(c + 2) % 3] = vread(c + 2);
+            if (c == 7) bp[rt] = *(const LDS_AS bf16x8_t*)(smem + (pb ^ 32) + rt * 32 * 64);
+            between(2 * c + rt);
+            __builtin_amdgcn_sched_barrier(0);  // keep the transfer between these two MFMAs
+          }
+        }
+      };
+
+      int lat = 3, rope = 2;
+      for (int h = h0 - 1; h0 < h1 && h < h1; ++h) {
+        const int lat1 = (lat + 1) & 3, latd = (lat + 3) & 3, rope1 = rope == 2 ? 0 : rope + 1;
+        // half page h + 1 landed: only the transfers of h + 2 may still be in flight
+        wait_vmcnt<kQDma>();
+        wg_barrier();
+        const int hd = h + 3;
+        const i32x4_t dr = step_rsrc(hd);
+        pv(h, kQLat + (h < h0 ? 0 : lat) * kQLatSlot, [&](int i) {
+          const int g = dma_at(i);
+          if (g >= 0) dma_piece_h(hd, dr, latd, rope, g);
+        });
+        lat = lat1;
+        rope = rope1;
+      }
+      // chunk end: normalise the 256 output dims of all 64 rows and store
+      // them through LDS (this wave's two latent slots), so that every store
+      // writes one whole 1 KB row segment.  Transfers past the chunk's end
+      // (empty ranges) write the slots: they land first.
+      wait_vmcnt<0>();
+      wg_barrier();  // 1 / l and offsets of every row visible; every wave is done with the slots
+      // staging row R (= tile row) holds 256 dims, 16-byte chunk c (dims 4c ..
+      // 4c + 3) at position c ^ (R & 7); lane base offsets recomputed per chunk
+      // (kept out of loop-invariant hoisting), the rest immediates
+      int wb[4], rb[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wb[j] = kQLat + wk * kQStage + l32 * 1024 + (((2 * j + hb) ^ (l32 & 7)) << 4);
+        asm volatile("" : "+v"(wb[j]));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        rb[i] = kQLat + wk * kQStage + ((lane ^ i) << 4);
+        asm volatile("" : "+v"(rb[i]));
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float inv = lbuf[32 * rt + l32];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const f32x16_t o = acc_out(O[dt][rt]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)  // chunk 8 dt + 2 j + hb
+            *(LDS_AS f32x4_t*)(smem + wb[j] + rt * 32 * 1024 + dt * 128) =
+                f32x4_t{o[4 * j] * inv, o[4 * j + 1] * inv, o[4 * j + 2] * inv, o[4 * j + 3] * inv};
+        }
+      }
+      // row R: every lane stores chunk `lane`; eight rows read before their stores
+      auto store_rows = [&](auto split_tag) {
+#pragma unroll
+        for (int k0 = 0; k0 < kQRows; k0 += 8) {
+          f32x4_t v[8];
+          int ro[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            v[i] = *(const LDS_AS f32x4_t*)(smem + rb[(k0 + i) & 7] + (k0 + i) * 1024);
+            ro[i] = rbuf[k0 + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (ro[i] >= 0) {
+              const long long d = (long long)ro[i] * kDv + 256 * wk + 4 * lane;
+              if constexpr (decltype(split_tag)::value) {
+                *(f32x4_t*)(p.o_acc + d) = v[i];
+              } else {
+                const u32x2_t pk = {pack_bf16(v[i][0], v[i][1]), pack_bf16(v[i][2], v[i][3])};
+                *(u32x2_t*)(p.out + d) = pk;
+              }
+            }
+          }
+        }
+      };
+      if (split) store_rows(std::true_type{});
+      else store_rows(std::false_type{});
+    }
+  }
+  // transfers past the last chunk's end (empty ranges) may still be in flight:
+  // let them land before the workgroup's LDS is released
+  wait_vmcnt<0>();
+}
+
+}  // namespace
+
+hipError_t launch_decode_qkpv(const DecodeParams& p, hipStream_t stream) {
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)decode_qkpv, hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
+  if (attr != hipSuccess) return attr;
+  const int grid = p.num_parts * p.m_tiles * p.h_kv;
+  hipLaunchKernelGGL(decode_qkpv, dim3(grid), dim3(kThreads), kQLds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

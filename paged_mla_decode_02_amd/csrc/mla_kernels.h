@@ -85,6 +85,8 @@ hipError_t launch_metadata(const int32_t* seqlens, int batch, int rows, int num_
                            int32_t* tile_md, int32_t* num_splits, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_wide(const DecodeParams& p, hipStream_t stream);
+// 64-row tiles on bf16 pages with score and value waves (decode_qkpv.hip)
+hipError_t launch_decode_qkpv(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* q_rope, const uint16_t* w_uk, int tokens,
                            int h_q, uint16_t* q_abs, hipStream_t stream);
