@@ -234,9 +234,13 @@ def test_random_shapes(env, seed):
                                f"causal={causal} P={P}")
 
 
-def test_large_scores_rescale(env):
-    """Scores far apart (|x| up to ~300 in log2 units) force the lazy rescale path."""
-    w = make_workload([3000, 640, 129], s_q=2, h_q=64, causal=True, seed=21)
+@pytest.mark.parametrize("h_q", [8, 16, 64, 128])
+def test_large_scores_rescale(env, h_q):
+    """Scores far apart (|x| up to ~300 in log2 units) force the lazy rescale
+    path of every kernel: 16 rows per KV head (token-split), 32 and 128 rows
+    (split-wave 64-row tiles, rescale threshold 2^64), 256 rows (128-row
+    tiles, 2^8)."""
+    w = make_workload([3000, 640, 129], s_q=2, h_q=h_q, causal=True, seed=21)
     ramp = np.linspace(0, 40, 3000 * 0 + w.num_pages * 64).astype(np.float32)
     kc = workloads.bf16_to_f32(w.kcache).reshape(w.num_pages * 64, -1)
     kc = kc * ramp[:, None]
