@@ -125,6 +125,21 @@ def test_decode_fp8_64row_tiles(env, lens, s_q, h_q, h_kv, causal, parts, sexp):
     check(go, gl, ro, rl, f"{lens} rows {s_q * h_q // h_kv}")
 
 
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_decode_fp8_long_chunk(env, h_q):
+    """One part holding a 157-page chunk (block-table entries fetched 64 at a
+    time inside the page loop) on FP8 pages: the 16-row and the 64-row kernel."""
+    _, _, orc, fp8, _, _ = env
+    w = make_workload([10000, 300], s_q=1, h_q=h_q, seed=950 + h_q)
+    kc8 = poison_tails(w, workloads.make_fp8_cache(w, seed=h_q))
+    go, gl = decode_fp8(env, w, kc8, num_parts=1)
+    clean = kc8.copy()
+    lat = clean[..., :512]
+    lat[lat == 0x7F] = 0
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(clean)))
+    check(go, gl, ro, rl, f"fp8 long chunk, {h_q} rows")
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_decode_fp8_64row_full_size(env, cfg):
     """compute_bound_full_heads (128 rows), spec_decode_causal (256 rows, causal)

@@ -167,6 +167,23 @@ def test_one_long_sequence(env, h_q):
     check(out, lse, *env[2].decode(w), what=f"2^20 tokens, {h_q} rows")
 
 
+@pytest.mark.parametrize("P", [1, 2])
+@pytest.mark.parametrize("s_q,h_q", [(1, 16), (1, 64), (1, 128), (2, 128)])
+def test_long_chunk_page_id_windows(env, s_q, h_q, P):
+    """Chunks of more than 64 pages in one part (a 10000-token sequence, 157
+    pages, with 1 or 2 parts): every kernel reads a sequence's block-table
+    entries 64 at a time and fetches the next 64 inside its page loop (16, 64,
+    128 and 256 rows per KV head)."""
+    w = make_workload([10000, 300], s_q=s_q, h_q=h_q, causal=s_q > 1, seed=900 + h_q + s_q,
+                      extra_pages=2, poison_tail=True, outliers=True)
+    md, ns, out, lse = run(env, w, num_parts=P)
+    md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
+    assert np.array_equal(md, md_ref) and np.array_equal(ns, ns_ref)
+    # the first part starts at page 0 of sequence 0 and ends more than 64 pages later
+    assert md[0, 0] == 0 and md[0, 1] == 0 and (md[0, 2] > 0 or md[0, 3] > 64)
+    check(out, lse, *env[2].decode(w), what=f"10000 tokens, {w.rows} rows, P={P}")
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # lens, s_q, h_q, h_kv, causal, num_parts

@@ -5,9 +5,10 @@ computes.  The kernels wait for their own transfers by count (the transfers are
 not visible to the compiler); a miscounted wait would let a wave read a page
 slot before its bytes land, which is a timing-dependent race that can pass a
 parity check by luck.  Here the arithmetic is identical, so out and lse must be
-bit-identical on every case: both decode kernels, bf16 and FP8 pages, the
-token-sparse gather, forced splits and ragged tiles.  Each pipelined result is
-also computed twice (run-to-run determinism of both kernels)."""
+bit-identical on every case: every decode kernel (16-row token-split, 64-row
+split-wave and pair-split, 128-row), bf16 and FP8 pages, the token-sparse
+gather, forced splits, ragged tiles and chunks longer than 64 pages.  Each
+pipelined result is also computed twice (run-to-run determinism)."""
 
 import numpy as np
 import pytest
@@ -76,6 +77,8 @@ CASES = [
     ([700, 900], 3, 32, 1, True, 11),
     ([5000], 1, 64, 1, False, 64),
     ([5000], 1, 16, 1, False, 64),
+    ([10000, 300], 1, 64, 1, False, 1),   # a 157-page chunk: page ids fetched inside the loop
+    ([10000], 2, 128, 1, True, 1),
 ]
 
 
