@@ -55,10 +55,13 @@ def test_noalloc_matches_decode_paged_calls_in_a_row(env):
     sizes.append(both(env, workloads.config_workload(4)))
     # smaller: memory_bound_varlen, 16 rows
     sizes.append(both(env, workloads.config_workload(1)))
+    # smaller again, forced splits, causal s_q = 2: 256 rows on the 128-row kernel
+    sizes.append(both(env, make_workload([700, 3, 129], s_q=2, h_q=128, causal=True, seed=7, outliers=True),
+                      num_parts=9))
     # smaller again, forced splits, causal s_q = 2 on the 64-row kernel
     sizes.append(both(env, make_workload([700, 3, 129], s_q=2, h_q=64, causal=True, seed=5, outliers=True),
                       num_parts=9))
-    assert sizes[0] > sizes[1] > sizes[2]
+    assert sizes[0] > sizes[1] > sizes[2] > sizes[3]
 
 
 def test_noalloc_rejects_a_call_beyond_the_scratch(env):
