@@ -7,6 +7,8 @@ maximum sizes (8192 sequences, a 2^20-token sequence), edge cases and random
 shapes.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -290,15 +292,21 @@ def test_page_permutation_bitwise(env, cfg, rows_h):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_out_of_range_page_ids_are_safe(env):
-    """An out-of-range page id reads as zeros instead of faulting."""
-    torch = env[0]
-    w = make_workload([200, 100], s_q=1, h_q=16, seed=4)
-    w.block_table[0, 1] = w.num_pages + 1000
+@pytest.mark.parametrize("bad", ["past_end", "negative"])
+@pytest.mark.parametrize("s_q,h_q", [(1, 16), (1, 64), (1, 128), (2, 128)])
+def test_out_of_range_page_ids_are_safe(env, s_q, h_q, bad):
+    """A block-table entry outside [0, num_pages) reads as a page of zeros in
+    every kernel (16, 64, 128 and 256 rows), never outside the cache: the
+    result equals the oracle's on the same table with that entry pointing at
+    an all-zero page appended to the cache."""
+    w = make_workload([200, 100], s_q=s_q, h_q=h_q, causal=s_q > 1, seed=4)
+    w.block_table[0, 1] = w.num_pages + 1000 if bad == "past_end" else -5
     _, _, out, lse = run(env, w)
-    go, gl = as_np(out, lse)
-    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
-    del torch
+    zero = np.zeros((1,) + w.kcache.shape[1:], dtype=w.kcache.dtype)
+    bt = w.block_table.copy()
+    bt[0, 1] = w.num_pages
+    ref = env[2].decode(dataclasses.replace(w, kcache=np.concatenate([w.kcache, zero]), block_table=bt))
+    check(out, lse, *ref, what=f"{bad} page id, {w.rows} rows")
 
 
 # ------------------------------------------------------------------ HIP graphs
