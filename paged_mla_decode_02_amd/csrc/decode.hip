@@ -78,30 +78,6 @@ __device__ __forceinline__ void dma_slice_fp8(LDS_AS char* dst, i32x4_t rsrc, co
   for (int k = 0; k < kF8SliceDma - 1; ++k) dma16(dst + 1024 * k, rsrc, d.off[k]);
   if (lane < kF8LastLanes) dma16(dst + 1024 * (kF8SliceDma - 1), rsrc, d.off[kF8SliceDma - 1]);
 }
-__device__ __forceinline__ unsigned cvt_fp8x2(unsigned v, float scale, bool hi_word) {
-  // e4m3 -> bf16 with a power-of-two scale (the instruction uses the scale's
-  // exponent), exact
-  return hi_word ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, true))
-                 : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, false));
-}
-// 8 e4m3 codes (two words) -> 8 bf16 times a power-of-two scale (exact)
-__device__ __forceinline__ bf16x8_t cvt8_fp8(unsigned w0, unsigned w1, float sc) {
-  const u32x4_t r = {cvt_fp8x2(w0, sc, false), cvt_fp8x2(w0, sc, true), cvt_fp8x2(w1, sc, false),
-                     cvt_fp8x2(w1, sc, true)};
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-// 8 bf16 values, element j times sc[j] (powers of two: exact while the
-// products stay in bf16's normal range)
-__device__ __forceinline__ bf16x8_t scale8(bf16x8_t v, const float* sc) {
-  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
-  u32x4_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = pack_bf16(__builtin_bit_cast(float, u[i] << 16) * sc[2 * i],
-                     __builtin_bit_cast(float, u[i] & 0xffff0000u) * sc[2 * i + 1]);
-  return __builtin_bit_cast(bf16x8_t, r);
-}
-typedef int i32x2_t __attribute__((ext_vector_type(2)));
 // Token-sparse decode.  A wave's 16-token slice of page blk of sequence b is
 // rows sp_offs[sp_rowptr[b] + 64 blk + 16 w + t], t < 16 (byte offsets; the
 // array is padded by one page, so a last page's reads stay inside it).  The 16
@@ -1097,7 +1073,6 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   DecodeParams q = p;
   q.m_tiles = pair_tiles_for(p.rows);
   q.xcd_map = (q.m_tiles * q.h_kv > 1 && q.num_parts % 8 == 0) ? 1 : 0;
-  if (q.kv_fp8) return launch_one<decode_pairsplit<false, true>>(kPsLds, q, stream);
   if (q.sparse) return launch_one<decode_pairsplit<true, false>>(kPsLds, q, stream);
   return launch_decode_qkpv(q, stream);
 }

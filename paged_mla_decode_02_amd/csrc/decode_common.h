@@ -92,6 +92,32 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
 }
 
+// FP8 (e4m3) cache rows, kF8RowBytes: conversions to bf16 MFMA operands.
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned cvt_fp8x2(unsigned v, float scale, bool hi_word) {
+  // e4m3 -> bf16 with a power-of-two scale (the instruction uses the scale's
+  // exponent), exact
+  return hi_word ? __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, true))
+                 : __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, scale, false));
+}
+// 8 e4m3 codes (two words) -> 8 bf16 times a power-of-two scale (exact)
+__device__ __forceinline__ bf16x8_t cvt8_fp8(unsigned w0, unsigned w1, float sc) {
+  const u32x4_t r = {cvt_fp8x2(w0, sc, false), cvt_fp8x2(w0, sc, true), cvt_fp8x2(w1, sc, false),
+                     cvt_fp8x2(w1, sc, true)};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+// 8 bf16 values, element j times sc[j] (powers of two: exact while the
+// products stay in bf16's normal range)
+__device__ __forceinline__ bf16x8_t scale8(bf16x8_t v, const float* sc) {
+  const u32x4_t u = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pack_bf16(__builtin_bit_cast(float, u[i] << 16) * sc[2 * i],
+                     __builtin_bit_cast(float, u[i] & 0xffff0000u) * sc[2 * i + 1]);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 __device__ __forceinline__ bf16x4_t lds_tr16(const LDS_AS char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4_t*)p);
 }

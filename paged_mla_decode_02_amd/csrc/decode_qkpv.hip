@@ -1,6 +1,6 @@
 // Paged MLA decode, 64-row tiles with two kinds of waves: the kernel for 17 to
-// 64 query rows per KV head on bf16 pages, and for each 64-row tile of 65 to
-// 128 rows.  Same method as decode.hip and decode_wide.hip -- every latent page
+// 64 query rows per KV head, and for each 64-row tile of more rows (65 to 128
+// on bf16 pages, any number on FP8 pages).  Same method as decode.hip and decode_wide.hip -- every latent page
 // read from HBM is multiplied against all query rows that share its KV head
 // ("OpenSourceWeek Day 1 -- Demystifying DeepSeek's FlashMLA",
 // deepseekonline.chat, §II.1), the softmax is computed online with a running
@@ -28,6 +28,16 @@
 // Page transfers, the slice swizzle and the chunk bookkeeping are those of
 // decode_common.h.  The lazy rescale is that of the other kernels with a
 // larger threshold (below).
+//
+// FP8 pages (656-byte rows, kF8RowBytes; decode_qkpv<true>): a half page's 32
+// rows move token-major, latent codes, group scales and rope together, into one
+// 20.5 KB slot (21 transfers, the value waves taking alternate ones).  The
+// score waves read each lane's K row in 16-byte chunks (two k-steps of 8 latent
+// codes, the query registers permuted to match), convert them to bf16 with the
+// token's group scale, and copy the half page's scales into an LDS table; the
+// value waves read V^T with the 8-bit transposed read and convert it without
+// scale, and fold each token's scale for the 128-dim group of an MFMA into the
+// P^T entries that multiply it (every scale is a power of two: exact).
 #include "decode_common.h"
 
 namespace mla {
@@ -57,21 +67,50 @@ static_assert(kQLds <= 160 * 1024, "LDS budget");
 // the sums below 2^64 times the key count: far inside the bf16 / fp32
 // exponent range (bf16 pages only: no FP8 scale multiplies P here).
 constexpr float kQTau = 64.0f;
+// (On FP8 pages P^T is multiplied by power-of-two group scales before PV: the
+// products stay finite while 2^64 times the values of V does, which the fp32
+// sums of O need on either kind of page.)
 
-// PV MFMA i of a step (0..31) is followed by transfer dma_at(i) of the next
-// half page but two, or by none (-1): the transfers spread evenly.
+// FP8 pages: four slots of 32 token-major 656-byte rows, inside the 128 KB the
+// chunk-end staging takes; P, alpha, the group-scale tables, 1 / l and the row
+// offsets after it.
+constexpr int kQF8Slot = kQHalf * kF8RowBytes;                         // 20992
+constexpr int kQF8Dma = (kQF8Slot + 1023) / 1024;                      // 21 transfers per half page
+constexpr int kQF8LastLanes = (kQF8Slot - 1024 * (kQF8Dma - 1)) / 16;  // the last one moves 32 x 16 B
+static_assert(4 * kQF8Slot <= 2 * kQStage, "FP8 slots inside the staging region");
+template <bool kFp8>
+struct QLay {
+  static constexpr int kSlot = kFp8 ? kQF8Slot : kQLatSlot;
+  static constexpr int kPbuf = kFp8 ? 2 * kQStage : kQPbuf;
+  static constexpr int kAbuf = kPbuf + 2 * kQPBytes;
+  static constexpr int kSbuf = kAbuf + 2 * kQRows * 4;  // FP8: 2 x scales [4 groups][32 tokens] fp32
+  static constexpr int kLbuf = kSbuf + (kFp8 ? 2 * 4 * kQHalf * 4 : 0);
+  static constexpr int kRbuf = kLbuf + kQRows * 4;
+  static constexpr int kLds = kRbuf + kQRows * 4;
+  // transfers per value wave wk per half page: 18 (bf16); FP8 transfers wk,
+  // wk + 2, .. of the 21
+  static constexpr int dmas(int wk) { return kFp8 ? (kQF8Dma + 1 - wk) / 2 : kQDma; }
+};
+static_assert(QLay<false>::kLds == kQLds && QLay<true>::kLds <= 160 * 1024, "LDS budget");
+
+// PV MFMA i of a step (0..31) is followed by transfer dma_at<n>(i) (of the n a
+// value wave issues) of the next half page but two, or by none (-1): the
+// transfers spread evenly.
+template <int N>
 __host__ __device__ constexpr int dma_at(int i) {
-  for (int g = 0; g < kQDma; ++g)
-    if ((32 * g) / kQDma == i) return g;
+  for (int g = 0; g < N; ++g)
+    if ((32 * g) / N == i) return g;
   return -1;
 }
 
+template <bool kFp8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_qkpv(DecodeParams p) {
+  using L = QLay<kFp8>;
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
-  LDS_AS float* lbuf = (LDS_AS float*)(smem + kQLbuf);
-  LDS_AS int* rbuf = (LDS_AS int*)(smem + kQRbuf);
+  LDS_AS float* lbuf = (LDS_AS float*)(smem + L::kLbuf);
+  LDS_AS int* rbuf = (LDS_AS int*)(smem + L::kRbuf);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -108,6 +147,12 @@ decode_qkpv(DecodeParams p) {
     const int pos = 2 * (g16 & 1) + ((k16 & 3) >> 1);
     vx = t * 128 + ((pos ^ swz(t)) << 4) + ((k16 & 1) << 3) + 4 * wk * kGroupBytes;
   }
+  // FP8 pages: the score waves read token l32's row; the value waves' 8-bit
+  // transposed V^T read of k-step ks, dim tile dt is at 16 ks rows + 32 dt
+  // bytes from vx8 (lanes 2k, 2k + 1 of a 16-lane group address token k of 8
+  // at +0 / +8 bytes, so lane i receives dim i of 8 consecutive tokens)
+  const int frow = l32 * kF8RowBytes;
+  const int vx8 = (8 * hb + (k16 >> 1)) * kF8RowBytes + 256 * wk + 16 * (g16 & 1) + 8 * (k16 & 1);
   // P^T operand of PV: row 32 rt + l32, tokens 16 ks + 8 hb .. +7: px ^ (ks << 5)
   const int px = wp_off(l32, hb);
   // P write of the softmax: row trow, tokens 8 j + 4 hb .. +3: (buffer + pwx) ^ (j << 4)
@@ -117,6 +162,22 @@ decode_qkpv(DecodeParams p) {
   // 16 wk + 15 of the first (d0) or second (d1) half of a page
   const SliceDma d0 = slice_dma_offsets(kSlice * wk, kvh, p.h_kv, lane);
   const SliceDma d1 = slice_dma_offsets(kQHalf + kSlice * wk, kvh, p.h_kv, lane);
+  // FP8 pages: transfer j of value wave wk is transfer n = wk + 2 j of a half
+  // page's 21; lane l supplies slot bytes 1024 n + 16 l, i.e. byte o - 656 t of
+  // row t = o / 656 (f8off: first half of a page; the second lies f8half
+  // further)
+  constexpr int kF8Mine = (kQF8Dma + 1) / 2;
+  int f8off[kF8Mine];
+  int f8half = 0;
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int j = 0; j < kF8Mine; ++j) {
+      const int o = 1024 * (wk + 2 * j) + 16 * lane;
+      const int t = min(o / kF8RowBytes, kQHalf - 1);  // lanes past the slot never transfer
+      f8off[j] = (t * p.h_kv + kvh) * kF8RowBytes + (o - t * kF8RowBytes);
+    }
+    f8half = kQHalf * p.h_kv * kF8RowBytes;
+  }
 
   for (int b = i0; b <= j0; ++b) {
     const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
@@ -133,22 +194,34 @@ decode_qkpv(DecodeParams p) {
     int ids = load_page_ids(p, b, sr.lo, lane);
     auto half_rsrc = [&](int h) {
       const int blk = h >> 1;
-      return page_rsrc(p, page_id(ids, (blk - sr.lo) & 63), blk, sr.L);
+      return page_rsrc(p, page_id(ids, (blk - sr.lo) & 63), blk, sr.L, kFp8 ? kF8RowBytes : kRowBytes);
     };
     // transfer i (0..17) of half page h by a value wave: chunk group i / 2
     // (group 8 is the rope part), token half i % 2
+    // (FP8 pages: transfer i of the wave's L::dmas(wk) into slot lat)
     auto dma_piece_h = [&](int h, i32x4_t r, int lat, int rope, int i) {
-      const int g = i >> 1, th = i & 1;
-      const int vb = ((h & 1) ? (th ? d1.vbase[1] : d1.vbase[0]) : (th ? d0.vbase[1] : d0.vbase[0])) + g * 128;
-      if (g < 8) dma16(smem + kQLat + lat * kQLatSlot + wk * kQLatSlice + g * kGroupBytes + th * 1024, r, vb);
-      else dma16(smem + kQRope + rope * kQRopeSlot + wk * kGroupBytes + th * 1024, r, vb);
+      if constexpr (kFp8) {
+        const int n = wk + 2 * i;
+        LDS_AS char* dst = smem + lat * kQF8Slot + 1024 * n;
+        const int src = f8off[i] + (h & 1) * f8half;
+        if (n < kQF8Dma - 1) dma16(dst, r, src);
+        else if (lane < kQF8LastLanes) dma16(dst, r, src);
+        (void)rope;
+      } else {
+        const int g = i >> 1, th = i & 1;
+        const int vb = ((h & 1) ? (th ? d1.vbase[1] : d1.vbase[0]) : (th ? d0.vbase[1] : d0.vbase[0])) + g * 128;
+        if (g < 8) dma16(smem + kQLat + lat * kQLatSlot + wk * kQLatSlice + g * kGroupBytes + th * 1024, r, vb);
+        else dma16(smem + kQRope + rope * kQRopeSlot + wk * kGroupBytes + th * 1024, r, vb);
+      }
     };
+    constexpr int kMaxDma = kFp8 ? kF8Mine : kQDma;
     auto prologue_dma = [&]() {
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const i32x4_t r = h0 + k < h1 ? half_rsrc(h0 + k) : make_rsrc(p.kcache, 0u);
 #pragma unroll
-        for (int g = 0; g < kQDma; ++g) dma_piece_h(h0 + k, r, k, k, g);
+        for (int g = 0; g < kMaxDma; ++g)
+          if (!kFp8 || g < L::dmas(wk)) dma_piece_h(h0 + k, r, k, k, g);
       }
     };
     // the resource of half page hd's transfers: past the chunk's end an empty
@@ -187,7 +260,8 @@ decode_qkpv(DecodeParams p) {
       {
         const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk);
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qreg[ks] = qp[2 * ks + hb];
+        for (int ks = 0; ks < 36; ++ks)  // FP8: latent k-step pairs follow the 16-byte code chunks
+          qreg[ks] = qp[kFp8 && ks < 32 ? 4 * (ks >> 1) + 2 * hb + (ks & 1) : 2 * ks + hb];
       }
       vm_drain();
       wg_barrier();  // every wave is done with the previous chunk's output staging in the slots
@@ -211,6 +285,40 @@ decode_qkpv(DecodeParams p) {
           S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S, 0, 0, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // FP8 pages: 20 reads per lane from token l32's row -- 16 latent chunks of
+      // 16 bytes (k-steps 2r and 2r + 1, converted with the token's group
+      // scale) and 4 rope k-steps of bf16; score wave 0 copies the row's four
+      // group scales into table tb for the value waves
+      auto qk8 = [&](int slot_off, int tb, f32x16_t& S) {
+        const LDS_AS char* krow = smem + slot_off + frow;
+        const f32x4_t sc = *(const LDS_AS f32x4_t*)(krow + kLatent);
+        if (wk == 0 && hb == 0) {
+          LDS_AS float* tab = (LDS_AS float*)(smem + L::kSbuf + tb * 4 * kQHalf * 4);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) tab[g * kQHalf + l32] = sc[g];
+        }
+        auto rd = [&](int r) {
+          return *(const LDS_AS u32x4_t*)(krow + (r < 16 ? 32 * r + 16 * hb : kLatent + 16 + 32 * (r - 16) + 16 * hb));
+        };
+        constexpr int kAheadR = 3;  // operand reads in flight ahead of their MFMAs
+        u32x4_t kr[kAheadR + 1];
+        S = f32x16_t{};
+#pragma unroll
+        for (int i = 0; i < kAheadR; ++i) kr[i] = rd(i);
+#pragma unroll
+        for (int r = 0; r < 20; ++r) {
+          if (r + kAheadR < 20) kr[(r + kAheadR) % (kAheadR + 1)] = rd(r + kAheadR);
+          const u32x4_t c = kr[r % (kAheadR + 1)];
+          if (r < 16) {
+            const float s8 = sc[r >> 2];
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8_fp8(c[0], c[1], s8), qreg[2 * r], S, 0, 0, 0);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8_fp8(c[2], c[3], s8), qreg[2 * r + 1], S, 0, 0, 0);
+          } else {
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c), qreg[16 + r], S, 0, 0, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -249,21 +357,28 @@ decode_qkpv(DecodeParams p) {
           sx[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sx[r], p.scale_log2, -m_use));
           psum += sx[r];
         }
-        const int pw = kQPbuf + (h & 1) * kQPBytes + pwx;
+        const int pw = L::kPbuf + (h & 1) * kQPBytes + pwx;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const u32x2_t v = {pack_bf16(sx[4 * j], sx[4 * j + 1]), pack_bf16(sx[4 * j + 2], sx[4 * j + 3])};
           *(LDS_AS u32x2_t*)(smem + (pw ^ (j << 4))) = v;
         }
         l_run += half_sum(psum);
-        if (hb == 0) ((LDS_AS float*)(smem + kQAbuf + (h & 1) * kQRows * 4))[trow] = alpha;
+        if (hb == 0) ((LDS_AS float*)(smem + L::kAbuf + (h & 1) * kQRows * 4))[trow] = alpha;
       };
 
       if (h0 < h1) {
-        const int pw = kQPbuf + ((h0 - 1) & 1) * kQPBytes + pwx;
+        const int pw = L::kPbuf + ((h0 - 1) & 1) * kQPBytes + pwx;
 #pragma unroll
         for (int j = 0; j < 4; ++j) *(LDS_AS u32x2_t*)(smem + (pw ^ (j << 4))) = u32x2_t{0u, 0u};
-        if (hb == 0) ((LDS_AS float*)(smem + kQAbuf + ((h0 - 1) & 1) * kQRows * 4))[trow] = 1.f;
+        if (hb == 0) ((LDS_AS float*)(smem + L::kAbuf + ((h0 - 1) & 1) * kQRows * 4))[trow] = 1.f;
+        if constexpr (kFp8) {  // finite scales for the first step's zero P
+          if (wk == 0 && hb == 0) {
+            LDS_AS float* tab = (LDS_AS float*)(smem + L::kSbuf + ((h0 - 1) & 1) * 4 * kQHalf * 4);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) tab[g * kQHalf + l32] = 0.f;
+          }
+        }
       }
       int lat = 3, rope = 2;
       for (int h = h0 - 1; h0 < h1 && h < h1; ++h) {
@@ -272,7 +387,8 @@ decode_qkpv(DecodeParams p) {
         wg_barrier();
         if (h + 1 < h1) {
           f32x16_t S;
-          qk(kQLat + lat1 * kQLatSlot, kQRope + rope1 * kQRopeSlot, S);
+          if constexpr (kFp8) qk8(lat1 * kQF8Slot, (h + 1) & 1, S);
+          else qk(kQLat + lat1 * kQLatSlot, kQRope + rope1 * kQRopeSlot, S);
           softmax(h + 1, S);
         }
         lat = lat1;
@@ -301,9 +417,9 @@ decode_qkpv(DecodeParams p) {
       // O^T [256 dims x 64 rows] += V^T . P^T over half page h's 32 tokens (value
       // waves); `between(i)` runs after the i-th of its 32 MFMAs
       auto pv = [&](int h, int lat_off, auto&& between) {
-        const LDS_AS float* ab = (const LDS_AS float*)(smem + kQAbuf + (h & 1) * kQRows * 4);
+        const LDS_AS float* ab = (const LDS_AS float*)(smem + L::kAbuf + (h & 1) * kQRows * 4);
         const float a0 = ab[l32], a1 = ab[32 + l32];
-        const int pb = kQPbuf + (h & 1) * kQPBytes + px;
+        const int pb = L::kPbuf + (h & 1) * kQPBytes + px;
         const int vb = lat_off + vx;
         // column c: k-step c / 8 (slice), dim tile c % 8
         auto vread = [&](int c) {
@@ -343,18 +459,94 @@ decode_qkpv(DecodeParams p) {
         }
       };
 
+      // FP8 pages: O^T [256 dims x 64 rows] += V^T . P^T over half page h, V^T
+      // through the 8-bit transposed read converted without scale; dim tiles
+      // 0..3 lie in scale group 2 wk, 4..7 in 2 wk + 1, and multiply P^T
+      // entries scaled by their tokens' scales of that group.  Every operand
+      // read is issued first; k-step 1's conversions run between k-step 0's
+      // MFMAs.
+      auto pv8 = [&](int h, int slot_off, auto&& between) {
+        const LDS_AS float* ab = (const LDS_AS float*)(smem + L::kAbuf + (h & 1) * kQRows * 4);
+        const float a0 = ab[l32], a1 = ab[32 + l32];
+        const int pb = L::kPbuf + (h & 1) * kQPBytes + px;
+        const LDS_AS float* tab = (const LDS_AS float*)(smem + L::kSbuf + (h & 1) * 4 * kQHalf * 4) + 8 * hb;
+        const LDS_AS char* vb = smem + slot_off + vx8;
+        i32x2_t vr[2][8];
+        bf16x8_t bp[2][2];
+        f32x4_t sr[2][4];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            vr[ks][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS i32x2_t*)(vb + 16 * ks * kF8RowBytes + 32 * dt));
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) bp[ks][rt] = *(const LDS_AS bf16x8_t*)(smem + (pb ^ (ks << 5)) + rt * 32 * 64);
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {  // tokens 16 ks + 8 hb .. +7 of group 2 wk + gi
+            sr[ks][2 * gi] = *(const LDS_AS f32x4_t*)(tab + (2 * wk + gi) * kQHalf + 16 * ks);
+            sr[ks][2 * gi + 1] = *(const LDS_AS f32x4_t*)(tab + (2 * wk + gi) * kQHalf + 16 * ks + 4);
+          }
+        }
+        if (__builtin_amdgcn_ballot_w64(a0 != 1.f || a1 != 1.f)) {
+          acc_settle(O[0][0]);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            acc_scale(O[dt][0], a0);
+            acc_scale(O[dt][1], a1);
+          }
+          asm volatile("s_nop 3" ::: "memory");
+        }
+        bf16x8_t va[2][8], bs[2][2][2];  // [k-step][dim tile], [k-step][group][row tile]
+        auto convert_v = [&](int ks, int dt) {
+          va[ks][dt] = cvt8_fp8((unsigned)vr[ks][dt][0], (unsigned)vr[ks][dt][1], 1.0f);
+        };
+        auto convert_p = [&](int ks, int gi, int rt) {
+          const float sv[8] = {sr[ks][2 * gi][0],     sr[ks][2 * gi][1],     sr[ks][2 * gi][2],
+                               sr[ks][2 * gi][3],     sr[ks][2 * gi + 1][0], sr[ks][2 * gi + 1][1],
+                               sr[ks][2 * gi + 1][2], sr[ks][2 * gi + 1][3]};
+          bs[ks][gi][rt] = scale8(bp[ks][rt], sv);
+        };
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) convert_v(0, dt);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) convert_p(0, q4 >> 1, q4 & 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+              pv_mfma(O[dt][rt], va[ks][dt], bs[ks][dt >> 2][rt]);
+              between(16 * ks + 2 * dt + rt);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            if (ks == 0) {
+              convert_v(1, dt);
+              if (dt < 4) convert_p(1, dt >> 1, dt & 1);
+            }
+          }
+        }
+      };
+
       int lat = 3, rope = 2;
       for (int h = h0 - 1; h0 < h1 && h < h1; ++h) {
         const int lat1 = (lat + 1) & 3, latd = (lat + 3) & 3, rope1 = rope == 2 ? 0 : rope + 1;
         // half page h + 1 landed: only the transfers of h + 2 may still be in flight
-        wait_vmcnt<kQDma>();
+        if constexpr (kFp8) {
+          if (wk == 0) wait_vmcnt<L::dmas(0)>();
+          else wait_vmcnt<L::dmas(1)>();
+        } else {
+          wait_vmcnt<kQDma>();
+        }
         wg_barrier();
         const int hd = h + 3;
         const i32x4_t dr = step_rsrc(hd);
-        pv(h, kQLat + (h < h0 ? 0 : lat) * kQLatSlot, [&](int i) {
-          const int g = dma_at(i);
-          if (g >= 0) dma_piece_h(hd, dr, latd, rope, g);
-        });
+        auto between = [&](int i) {
+          const int g = dma_at<kMaxDma>(i);
+          if (g >= 0 && (!kFp8 || g < L::dmas(wk))) dma_piece_h(hd, dr, latd, rope, g);
+        };
+        if constexpr (kFp8) pv8(h, (h < h0 ? 0 : lat) * kQF8Slot, between);
+        else pv(h, kQLat + (h < h0 ? 0 : lat) * kQLatSlot, between);
         lat = lat1;
         rope = rope1;
       }
@@ -424,15 +616,21 @@ decode_qkpv(DecodeParams p) {
   wait_vmcnt<0>();
 }
 
+template <bool kFp8>
+hipError_t launch_qkpv(const DecodeParams& p, hipStream_t stream) {
+  constexpr int lds = QLay<kFp8>::kLds;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)decode_qkpv<kFp8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  const int grid = p.num_parts * p.m_tiles * p.h_kv;
+  hipLaunchKernelGGL(decode_qkpv<kFp8>, dim3(grid), dim3(kThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode_qkpv(const DecodeParams& p, hipStream_t stream) {
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)decode_qkpv, hipFuncAttributeMaxDynamicSharedMemorySize, kQLds);
-  if (attr != hipSuccess) return attr;
-  const int grid = p.num_parts * p.m_tiles * p.h_kv;
-  hipLaunchKernelGGL(decode_qkpv, dim3(grid), dim3(kThreads), kQLds, stream, p);
-  return hipGetLastError();
+  return p.kv_fp8 ? launch_qkpv<true>(p, stream) : launch_qkpv<false>(p, stream);
 }
 
 }  // namespace mla
