@@ -31,18 +31,19 @@
 //     units), so the O rescale is rare; the final normalisation uses the same
 //     reference max, which keeps the result exact up to rounding.
 //
-// Two kernels:
+// Two kernels here (and the dispatch over all of them; the 64-row tiles of
+// paged pages are decode_qkpv.hip's, the 128-row tiles decode_wide.hip's):
 //   decode_tokensplit  (<= 16 query rows per KV head, memory-bound shapes):
 //     each of the 4 waves owns 16 tokens of every page and an independent online
 //     softmax over them; the 4 states merge at the end of a chunk through LDS.
-//   decode_pairsplit  (64-row tiles, compute-bound shapes):
-//     QK^T is split 2 x 2 over rows and tokens (32 rows per wave, queries
-//     resident in registers), P goes through LDS, and PV is split by output dims
-//     (128 per wave), so each V element of a page is read from LDS once per
-//     workgroup.
-// Both also run on the FP8 cache (656-byte rows, see kF8RowBytes): pages stay
-// FP8 in LDS and the MFMA operands are dequantised in registers, K with its
-// per-group scale and V without, the V scale folded into P.
+//     It also runs on the FP8 cache (656-byte rows, see kF8RowBytes): pages
+//     stay FP8 in LDS and the MFMA operands are dequantised in registers, K
+//     with its per-group scale and V without, the V scale folded into P.
+//   decode_pairsplit  (64-row tiles of gathered rows: the token-sparse decode
+//     of more than 16 rows per KV head): QK^T is split 2 x 2 over rows and
+//     tokens (32 rows per wave, queries resident in registers), P goes through
+//     LDS, and PV is split by output dims (128 per wave), so each V element of
+//     a page is read from LDS once per workgroup.
 #include <type_traits>
 #include <utility>
 
@@ -540,18 +541,17 @@ decode_tokensplit(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// 64-row tiles: pair-split kernel.
+// 64-row tiles of gathered rows (token-sparse decode): pair-split kernel.
 // The 4 waves form a 2 x 2 grid: wave w owns query rows 32*(w&1) .. +31 (its
 // queries stay in registers) and tokens 32*(w>>1) .. +31 of every page for
 // QK^T.  The two waves of a row group agree on one running max per page through
 // LDS, so their P blocks share a reference; P goes to LDS and PV is split by
 // output dims (128 per wave, all 64 rows), which reads every V element of the
 // page from LDS once per workgroup.
-// LDS: two page buffers (bf16 pages, or FP8 pages in their first 82 KB), P
-// [64 rows x 64 tokens] bf16, the per-page row maxima of both token groups,
-// alpha, the end-of-chunk (m, l) of both token groups, the token-sparse row
-// offsets and the FP8 page's scale table.  At a chunk end the page buffers
-// stage each wave's output rows.
+// LDS: two page buffers, P [64 rows x 64 tokens] bf16, the per-page row maxima
+// of both token groups, alpha, the end-of-chunk (m, l) of both token groups and
+// the gathered rows' byte offsets.  At a chunk end the page buffers stage each
+// wave's output rows.
 constexpr int kPsRows = 64;
 constexpr int kPsPbuf = 2 * kPageBytes;
 constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
@@ -563,8 +563,7 @@ constexpr int kPsOffs = kPsSbuf + 2 * kPsRows * 2 * 4;  // token-sparse: [2 page
 constexpr int kPsStgStride = 132;
 constexpr int kPsStgBytes = kPsRows * kPsStgStride * 4 + kPsRows * 8;
 static_assert(4 * kPsStgBytes <= kPsPbuf, "the chunk-end staging must fit in the page buffers");
-constexpr int kPsScl = kPsOffs + 2 * 4 * kSlice * 4;    // FP8 pages: [4 groups][64 tokens] fp32 scales of the page
-constexpr int kPsLds = kPsScl + 4 * kPage * 4;
+constexpr int kPsLds = kPsOffs + 2 * 4 * kSlice * 4;
 // transfer pieces of the next page issued during QK^T (the rest during PV)
 #ifndef MLA_QK_DMA
 #define MLA_QK_DMA 18
@@ -583,38 +582,9 @@ constexpr int kPvDma0 = kQkDma + kSmDma;
 // chunk on 16 different bank groups.
 __device__ __forceinline__ int pbuf_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-// FP8 pages in the 64-row kernel.  A page lives in LDS as its 64 token-major
-// 656-byte rows: 41 transfers of 1 KB, wave w issuing transfers w, w + 4, ...
-// Rows 656 bytes apart put 16 consecutive tokens on 16 distinct 16-byte bank
-// groups, so the K operand reads (16 bytes of one token per lane) and the
-// transposed V reads are conflict free without a swizzle.
-constexpr int kF8PageBytes = kPage * kF8RowBytes;  // 41984
-constexpr int kF8PageDma = kF8PageBytes / 1024;     // 41
-constexpr int kF8WaveDma = (kF8PageDma + 3) / 4;    // 11 (waves 1-3 issue 10)
-static_assert(kF8PageBytes % 1024 == 0, "an FP8 page is a whole number of transfers");
-struct PageDmaF8 {
-  int off[kF8WaveDma];
-};
-__device__ __forceinline__ PageDmaF8 fp8_page_dma_offsets(int w, int kvh, int h_kv, int lane) {
-  PageDmaF8 d;
-#pragma unroll
-  for (int i = 0; i < kF8WaveDma; ++i) {
-    const int o = 1024 * (w + 4 * i) + 16 * lane;  // byte of the LDS page image
-    const int t = o / kF8RowBytes;                 // its token and byte within the row
-    d.off[i] = (t * h_kv + kvh) * kF8RowBytes + (o - t * kF8RowBytes);
-  }
-  return d;
-}
-// transfer i of wave w's share of an FP8 page
-__device__ __forceinline__ void dma_piece_f8(LDS_AS char* page, i32x4_t rsrc, const PageDmaF8& d, int w, int i) {
-  if (w + 4 * i < kF8PageDma) dma16(page + 1024 * (w + 4 * i), rsrc, d.off[i]);
-}
-
-template <bool kSparse, bool kFp8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_pairsplit(DecodeParams p) {
-  static_assert(!(kSparse && kFp8), "the token-sparse decode reads bf16 rows");
-  constexpr int kPg = kFp8 ? kF8PageBytes : kPageBytes;  // LDS bytes of one page
+  constexpr int kPg = kPageBytes;  // LDS bytes of one page
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
   LDS_AS char* pages = smem;
@@ -622,7 +592,6 @@ decode_pairsplit(DecodeParams p) {
   LDS_AS float* xmax = (LDS_AS float*)(smem + kPsXmax);  // [2 token groups][64 rows]
   LDS_AS float* abuf = (LDS_AS float*)(smem + kPsAbuf);  // [64 rows]
   LDS_AS float* sbuf = (LDS_AS float*)(smem + kPsSbuf);  // [2 token groups][64 rows][2]
-  LDS_AS float* scl = (LDS_AS float*)(smem + kPsScl);    // FP8 pages: [4 groups][64 tokens]
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -666,20 +635,7 @@ decode_pairsplit(DecodeParams p) {
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) paddr[rt][ks] = pbuf_off(rt * 32 + l32, 2 * ks + hb);
-  const SliceDma dma = slice_dma_offsets(w * kSlice, kvh, p.h_kv, lane);
-  // FP8 pages: the K operand row of this lane's token; the transposed V read of
-  // lanes 2k, 2k+1 of a 16-lane group addresses token k of the group's 8 at
-  // bytes +0 / +8, so that lane i receives dim i of 8 consecutive tokens
-  // (16 tokens per k-step: 8 * hb + k16 / 2; dims 128 w + 32 dt + 16 (g16 & 1) + k16)
-  int frow = 0, vaddr8 = 0;
-  PageDmaF8 fdma = {};
-  if constexpr (kFp8) {
-    frow = (32 * tg + l32) * kF8RowBytes;
-    vaddr8 = (8 * hb + (k16 >> 1)) * kF8RowBytes + 128 * w + 16 * (g16 & 1) + 8 * (k16 & 1);
-    fdma = fp8_page_dma_offsets(w, kvh, p.h_kv, lane);
-  }
-  i32x4_t offs_rsrc = {};
-  if constexpr (kSparse) offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);  // the row-offset list
+  const i32x4_t offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);  // the row-offset list
 
   for (int b = i0; b <= j0; ++b) {
     const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
@@ -689,14 +645,11 @@ decode_pairsplit(DecodeParams p) {
     const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
 
     // rows past the last one compute on row 0's query and are never stored
-    // (FP8 pages: k-steps 2j, 2j+1 of the latent take bytes 0-7 / 8-15 of the
-    // 16-byte chunk 32 j + 16 hb, i.e. dims 32 j + 16 hb + 8 (ks & 1) .. +7)
     bf16x8_t qreg[36];
     {
       const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk);
 #pragma unroll
-      for (int ks = 0; ks < 36; ++ks)
-        qreg[ks] = qp[kFp8 && ks < 32 ? 4 * (ks >> 1) + 2 * hb + (ks & 1) : 2 * ks + hb];
+      for (int ks = 0; ks < 36; ++ks) qreg[ks] = qp[2 * ks + hb];
     }
     f32x16_t O[4][2];
 #pragma unroll
@@ -705,31 +658,15 @@ decode_pairsplit(DecodeParams p) {
 
     // token-sparse: the sequence's rows are listed, not paged; the offsets of
     // page blk + 1 are staged one page ahead (LDS slot by page parity)
-    i32x4_t grsrc = {};
-    if constexpr (kSparse) grsrc = make_rsrc(p.kcache, p.sp_cache_bytes);
+    const i32x4_t grsrc = make_rsrc(p.kcache, p.sp_cache_bytes);
     const auto slice_valid = [&](int blk_) { return min(max(sr.L - blk_ * kPage - w * kSlice, 0), kSlice); };
     LDS_AS char* offs_slot[2] = {smem + kPsOffs + w * 64, smem + kPsOffs + (4 + w) * 64};
-    int row0 = 0;
-    int ids = -1;
-    if constexpr (kSparse) {
-      row0 = ((const CONST_AS int32_t*)p.sp_rowptr)[b];
-      if (sr.lo < sr.hi) {
-        stage_offs(offs_slot[0], offs_rsrc, row0, sr.lo, w, lane);
-        if (sr.lo + 1 < sr.hi) stage_offs(offs_slot[1], offs_rsrc, row0, sr.lo + 1, w, lane);
-        wait_vmcnt<0>();
-        dma_slice(pages + w * kSliceBytes, grsrc, gathered_dma(offs_slot[0], slice_valid(sr.lo), kvh, lane));
-      }
-    } else {
-      ids = load_page_ids(p, b, sr.lo, lane);
-      if (sr.lo < sr.hi) {
-        if constexpr (kFp8) {
-          const i32x4_t r = page_rsrc(p, page_id(ids, 0), sr.lo, sr.L, kF8RowBytes);
-#pragma unroll
-          for (int i = 0; i < kF8WaveDma; ++i) dma_piece_f8(pages, r, fdma, w, i);
-        } else {
-          dma_slice(pages + w * kSliceBytes, page_rsrc(p, page_id(ids, 0), sr.lo, sr.L), dma);
-        }
-      }
+    const int row0 = ((const CONST_AS int32_t*)p.sp_rowptr)[b];
+    if (sr.lo < sr.hi) {
+      stage_offs(offs_slot[0], offs_rsrc, row0, sr.lo, w, lane);
+      if (sr.lo + 1 < sr.hi) stage_offs(offs_slot[1], offs_rsrc, row0, sr.lo + 1, w, lane);
+      wait_vmcnt<0>();
+      dma_slice(pages + w * kSliceBytes, grsrc, gathered_dma(offs_slot[0], slice_valid(sr.lo), kvh, lane));
     }
     for (int blk = sr.lo; blk < sr.hi; ++blk) {
       const int pb = (blk - sr.lo) & 1;
@@ -741,18 +678,12 @@ decode_pairsplit(DecodeParams p) {
       LDS_AS char* npage = pages + (pb ^ 1) * kPg;
       LDS_AS char* ndst = npage + w * kSliceBytes;
       i32x4_t nrsrc = {0, 0, 0, 0};
-      SliceDma ndma = dma;
+      SliceDma ndma = {};
       if (has_next) {
-        if constexpr (kSparse) {
-          const int ns = (blk + 1 - sr.lo) & 1;
-          nrsrc = grsrc;
-          ndma = gathered_dma(offs_slot[ns], slice_valid(blk + 1), kvh, lane);
-          if (blk + 2 < sr.hi) stage_offs(offs_slot[ns ^ 1], offs_rsrc, row0, blk + 2, w, lane);
-        } else {
-          const int k = (blk + 1 - sr.lo) & 63;
-          if (k == 0) ids = load_page_ids(p, b, blk + 1, lane);
-          nrsrc = page_rsrc(p, page_id(ids, k), blk + 1, sr.L, kFp8 ? kF8RowBytes : kRowBytes);
-        }
+        const int ns = (blk + 1 - sr.lo) & 1;
+        nrsrc = grsrc;
+        ndma = gathered_dma(offs_slot[ns], slice_valid(blk + 1), kvh, lane);
+        if (blk + 2 < sr.hi) stage_offs(offs_slot[ns ^ 1], offs_rsrc, row0, blk + 2, w, lane);
       }
       const LDS_AS char* page = pages + pb * kPg;
 
@@ -784,52 +715,9 @@ decode_pairsplit(DecodeParams p) {
         }
         return S0 + S1;
       };
-      // FP8 pages: 20 operand reads per lane -- 16 latent chunks of 16 bytes (two
-      // k-steps each, dequantised with the token's group scale) and 4 rope
-      // k-steps of bf16 -- and the next page's kF8WaveDma transfers spread over them
-      auto qk8 = [&](auto with_dma) {
-        f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
-        const LDS_AS char* krow = page + frow;
-        const f32x4_t sc = *(const LDS_AS f32x4_t*)(krow + kLatent);  // the token's 4 group scales
-        if (rg == 0 && hb == 0) {  // waves 0 and 2 hold every token once: the PV waves' table
-#pragma unroll
-          for (int g = 0; g < 4; ++g) scl[g * kPage + 32 * tg + l32] = sc[g];
-        }
-        auto rd = [&](int r) {
-          return *(const LDS_AS u32x4_t*)(krow + (r < 16 ? 32 * r + 16 * hb : kLatent + 16 + 32 * (r - 16) + 16 * hb));
-        };
-        constexpr int kAheadR = 3;  // operand reads in flight ahead of their MFMAs
-        u32x4_t kr[kAheadR + 1];
-#pragma unroll
-        for (int i = 0; i < kAheadR; ++i) kr[i] = rd(i);
-#pragma unroll
-        for (int r = 0; r < 20; ++r) {
-          if (r + kAheadR < 20) kr[(r + kAheadR) % (kAheadR + 1)] = rd(r + kAheadR);
-          const u32x4_t c = kr[r % (kAheadR + 1)];
-          if (r < 16) {
-            const float s8 = sc[r >> 2];
-            S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8_fp8(c[0], c[1], s8), qreg[2 * r], S0, 0, 0, 0);
-            S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cvt8_fp8(c[2], c[3], s8), qreg[2 * r + 1], S1, 0, 0, 0);
-          } else {
-            const int ks = 32 + (r - 16);
-            if (ks & 1) S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c), qreg[ks], S1, 0, 0, 0);
-            else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c), qreg[ks], S0, 0, 0, 0);
-          }
-          if constexpr (decltype(with_dma)::value) {
-#pragma unroll
-            for (int i = r * kF8WaveDma / 20; i < (r + 1) * kF8WaveDma / 20; ++i) dma_piece_f8(npage, nrsrc, fdma, w, i);
-          }
-        }
-        return S0 + S1;
-      };
       f32x16_t S;
-      if constexpr (kFp8) {
-        if (has_next) S = qk8(std::true_type{});
-        else S = qk8(std::false_type{});
-      } else {
-        if (has_next) S = qk(std::true_type{});
-        else S = qk(std::false_type{});
-      }
+      if (has_next) S = qk(std::true_type{});
+      else S = qk(std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
       // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page.
       // Scores stay unscaled (the scale is positive, so the max commutes with
@@ -860,7 +748,7 @@ decode_pairsplit(DecodeParams p) {
       for (int r = 0; r < 16; ++r) {
         S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -m_use));
         ps += S[r];
-        if (!kFp8 && kSmDma > 0 && has_next && r % 4 == 3) {
+        if (kSmDma > 0 && has_next && r % 4 == 3) {
           for (int i = kQkDma + (r / 4) * kSmDma / 4; i < kQkDma + (r / 4 + 1) * kSmDma / 4; ++i)
             dma_piece(ndst, nrsrc, ndma, i);
         }
@@ -886,94 +774,47 @@ decode_pairsplit(DecodeParams p) {
           }
         }
       }
-      if constexpr (kFp8) {
-        // FP8 pages: V^T through the 8-bit transposed read, dequantised without
-        // scale; wave w's 128 dims are exactly latent group w, so each token's
-        // group-w scale multiplies its P^T entries instead.  The operands of
-        // k-step ks + 1 are read and converted while the MFMAs of k-step ks run.
-        const LDS_AS float* sclw = scl + w * kPage + 8 * hb;
-        bf16x8_t bp[4][2];
+      // operands of k-step ks (16 tokens): P^T for both row tiles and V^T for the
+      // four 32-dim tiles; the next k-step's operands load while this one's
+      // MFMAs run
+      struct PvOps {
+        bf16x8_t bp[2];
+        bf16x8_t va[4];
+      };
+      auto load_ops = [&](int ks) {
+        PvOps o;
+        o.bp[0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
+        o.bp[1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
+        const LDS_AS char* vs = page + ks * kSliceBytes;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          bp[ks][0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
-          bp[ks][1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
+        for (int dt = 0; dt < 4; ++dt) {
+          const int go = (dt >> 1) * kGroupBytes;
+          const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
+          const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
+          o.va[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-        i32x2_t vr[2][4];
-        f32x4_t sr[2][2];
-        auto read_ops = [&](int ks, int slot) {
+        return o;
+      };
+      PvOps ops[2];
+      ops[0] = load_ops(0);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            vr[slot][dt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (LDS_AS i32x2_t*)(page + 16 * ks * kF8RowBytes + 32 * dt + vaddr8));
-          sr[slot][0] = *(const LDS_AS f32x4_t*)(sclw + 16 * ks);
-          sr[slot][1] = *(const LDS_AS f32x4_t*)(sclw + 16 * ks + 4);
-        };
-        bf16x8_t va[2][4], bs[2][2];
-        auto convert_ops = [&](int ks, int slot) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) va[slot][dt] = cvt8_fp8((unsigned)vr[slot][dt][0], (unsigned)vr[slot][dt][1], 1.0f);
-          const float sv[8] = {sr[slot][0][0], sr[slot][0][1], sr[slot][0][2], sr[slot][0][3],
-                               sr[slot][1][0], sr[slot][1][1], sr[slot][1][2], sr[slot][1][3]};
-          bs[slot][0] = scale8(bp[ks][0], sv);
-          bs[slot][1] = scale8(bp[ks][1], sv);
-        };
-        read_ops(0, 0);
-        convert_ops(0, 0);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int cur = ks & 1;
-          if (ks + 1 < 4) read_ops(ks + 1, cur ^ 1);
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cur][dt], bs[cur][0], O[dt][0], 0, 0, 0);
-            O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cur][dt], bs[cur][1], O[dt][1], 0, 0, 0);
-          }
-          if (ks + 1 < 4) convert_ops(ks + 1, cur ^ 1);
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) {
+          ops[(ks + 1) & 1] = load_ops(ks + 1);
         }
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        // operands of k-step ks (16 tokens): P^T for both row tiles and V^T for the
-        // four 32-dim tiles; the next k-step's operands load while this one's
-        // MFMAs run
-        struct PvOps {
-          bf16x8_t bp[2];
-          bf16x8_t va[4];
-        };
-        auto load_ops = [&](int ks) {
-          PvOps o;
-          o.bp[0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
-          o.bp[1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
-          const LDS_AS char* vs = page + ks * kSliceBytes;
+        const PvOps& o = ops[ks & 1];
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int go = (dt >> 1) * kGroupBytes;
-            const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
-            const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
-            o.va[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          }
-          return o;
-        };
-        PvOps ops[2];
-        ops[0] = load_ops(0);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          if (ks + 1 < 4) {
-            ops[(ks + 1) & 1] = load_ops(ks + 1);
-          }
-          const PvOps& o = ops[ks & 1];
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
-            O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
-          }
-          if (has_next) {
-            for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
-                 ++i)
-              dma_piece(ndst, nrsrc, ndma, i);
-          }
+        for (int dt = 0; dt < 4; ++dt) {
+          O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
+          O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if (has_next) {
+          for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
+               ++i)
+            dma_piece(ndst, nrsrc, ndma, i);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- epilogue: (m, l) of both token groups for every row
@@ -1069,11 +910,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     return launch_one<decode_tokensplit<false>>(TsLayout<false>::kLds, p, stream);
   }
   if (tile_rows_for(p.rows) == 128 && !p.kv_fp8 && !p.sparse) return launch_decode_wide(p, stream);
-  // 64-row tiles (for any row count on FP8 pages and gathered rows)
+  // 64-row tiles (any row count on FP8 pages and gathered rows): the pair-split
+  // kernel for gathered rows, the split-wave kernel for pages
   DecodeParams q = p;
   q.m_tiles = pair_tiles_for(p.rows);
   q.xcd_map = (q.m_tiles * q.h_kv > 1 && q.num_parts % 8 == 0) ? 1 : 0;
-  if (q.sparse) return launch_one<decode_pairsplit<true, false>>(kPsLds, q, stream);
+  if (q.sparse) return launch_one<decode_pairsplit>(kPsLds, q, stream);
   return launch_decode_qkpv(q, stream);
 }
 

@@ -77,11 +77,17 @@ constexpr float kQTau = 64.0f;
 constexpr int kQF8Slot = kQHalf * kF8RowBytes;                         // 20992
 constexpr int kQF8Dma = (kQF8Slot + 1023) / 1024;                      // 21 transfers per half page
 constexpr int kQF8LastLanes = (kQF8Slot - 1024 * (kQF8Dma - 1)) / 16;  // the last one moves 32 x 16 B
-static_assert(4 * kQF8Slot <= 2 * kQStage, "FP8 slots inside the staging region");
+// four, as on bf16 pages: five to seven (three to five half pages in flight
+// instead of two) measured the same, the FP8 steps being bound by the waves'
+// work rather than by the page stream
+constexpr int kQF8Slots = 4;
 template <bool kFp8>
 struct QLay {
   static constexpr int kSlot = kFp8 ? kQF8Slot : kQLatSlot;
-  static constexpr int kPbuf = kFp8 ? 2 * kQStage : kQPbuf;
+  // half-page slots: step h reads slots h (PV) and h + 1 (QK^T) and requests
+  // half page h + kSlots - 1 into the slot h - 1 left
+  static constexpr int kSlots = kFp8 ? kQF8Slots : 4;
+  static constexpr int kPbuf = kFp8 ? (kSlots * kQF8Slot > 2 * kQStage ? kSlots * kQF8Slot : 2 * kQStage) : kQPbuf;
   static constexpr int kAbuf = kPbuf + 2 * kQPBytes;
   static constexpr int kSbuf = kAbuf + 2 * kQRows * 4;  // FP8: 2 x scales [4 groups][32 tokens] fp32
   static constexpr int kLbuf = kSbuf + (kFp8 ? 2 * 4 * kQHalf * 4 : 0);
@@ -217,7 +223,7 @@ decode_qkpv(DecodeParams p) {
     constexpr int kMaxDma = kFp8 ? kF8Mine : kQDma;
     auto prologue_dma = [&]() {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
+      for (int k = 0; k < L::kSlots - 2; ++k) {
         const i32x4_t r = h0 + k < h1 ? half_rsrc(h0 + k) : make_rsrc(p.kcache, 0u);
 #pragma unroll
         for (int g = 0; g < kMaxDma; ++g)
@@ -380,9 +386,10 @@ decode_qkpv(DecodeParams p) {
           }
         }
       }
-      int lat = 3, rope = 2;
+      int lat = L::kSlots - 1, rope = 2;
       for (int h = h0 - 1; h0 < h1 && h < h1; ++h) {
-        const int lat1 = (lat + 1) & 3, rope1 = rope == 2 ? 0 : rope + 1;
+        const int lat1 = kFp8 ? (lat + 1 == L::kSlots ? 0 : lat + 1) : (lat + 1) & 3;
+        const int rope1 = rope == 2 ? 0 : rope + 1;
         // half page h + 1 landed (the value waves wait for their transfers before it)
         wg_barrier();
         if (h + 1 < h1) {
@@ -528,18 +535,21 @@ decode_qkpv(DecodeParams p) {
         }
       };
 
-      int lat = 3, rope = 2;
+      int lat = L::kSlots - 1, rope = 2;
       for (int h = h0 - 1; h0 < h1 && h < h1; ++h) {
-        const int lat1 = (lat + 1) & 3, latd = (lat + 3) & 3, rope1 = rope == 2 ? 0 : rope + 1;
-        // half page h + 1 landed: only the transfers of h + 2 may still be in flight
+        const int lat1 = kFp8 ? (lat + 1 == L::kSlots ? 0 : lat + 1) : (lat + 1) & 3;
+        const int latd = kFp8 ? (lat == 0 ? L::kSlots - 1 : lat - 1) : (lat + 3) & 3;
+        const int rope1 = rope == 2 ? 0 : rope + 1;
+        // half page h + 1 landed: only the transfers of h + 2 .. h + kSlots - 2
+        // may still be in flight
         if constexpr (kFp8) {
-          if (wk == 0) wait_vmcnt<L::dmas(0)>();
-          else wait_vmcnt<L::dmas(1)>();
+          if (wk == 0) wait_vmcnt<(L::kSlots - 3) * L::dmas(0)>();
+          else wait_vmcnt<(L::kSlots - 3) * L::dmas(1)>();
         } else {
           wait_vmcnt<kQDma>();
         }
         wg_barrier();
-        const int hd = h + 3;
+        const int hd = h + L::kSlots - 1;
         const i32x4_t dr = step_rsrc(hd);
         auto between = [&](int i) {
           const int g = dma_at<kMaxDma>(i);

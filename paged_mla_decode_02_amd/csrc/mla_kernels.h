@@ -23,7 +23,7 @@ constexpr int kF8Group = 128;
 constexpr int kF8RowBytes = kLatent + 4 * (kLatent / kF8Group) + 2 * kRope;
 
 // Query rows one workgroup owns: <= 16 rows use the 16-row token-split kernel,
-// up to 128 rows the 64-row pair-split kernel (ceil(rows / 64) row tiles),
+// up to 128 rows the 64-row split-wave kernel (ceil(rows / 64) row tiles),
 // more the 128-row kernel (ceil(rows / 128) row tiles).  At 128 rows the
 // 128-row kernel would need twice the parts to fill the GPU, and the extra
 // split partials cost more than its faster tile saves.  The FP8 and

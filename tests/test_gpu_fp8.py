@@ -9,7 +9,7 @@
 The FP8 caches are drawn directly in the format (workloads.make_fp8_cache), and
 slots past a sequence's end hold NaN codes, which must never reach a result.
 Both decode kernels are covered: up to 16 rows per KV head (token-split) and
-64-row tiles (pair-split), with scales from 2^-13 to 2^13.
+64-row tiles (split-wave), with scales from 2^-13 to 2^13.
 """
 import dataclasses
 

@@ -137,7 +137,7 @@ def test_large_configs_full(env, cfg):
 def test_combine_more_than_256_chunks(env, h_q, L):
     """One sequence cut into ~290 chunks (300 parts): the combine stages chunk
     weights 256 at a time, so its second tile runs.  16 rows (token-split
-    kernel) and 64 rows (pair-split kernel), every row against the oracle."""
+    kernel) and 64 rows (split-wave kernel), every row against the oracle."""
     w = make_workload([L], s_q=1, h_q=h_q, seed=90 + h_q, outliers=True)
     md, ns, out, lse = run(env, w, num_parts=300)
     md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
@@ -160,7 +160,7 @@ def test_max_batch(env):
 @pytest.mark.parametrize("h_q", [16, 64])
 def test_one_long_sequence(env, h_q):
     """One sequence of 2^20 tokens (16384 pages, split across every part), 16
-    rows (token-split kernel) and 64 rows (pair-split kernel)."""
+    rows (token-split kernel) and 64 rows (split-wave kernel)."""
     w = make_workload([1 << 20], s_q=1, h_q=h_q, seed=82 + h_q)
     md, ns, out, lse = run(env, w)
     md_ref, ns_ref = env[2].schedule(w.cache_seqlens, w.rows, md.shape[0])
