@@ -140,6 +140,28 @@ def test_decode_fp8_long_chunk(env, h_q):
     check(go, gl, ro, rl, f"fp8 long chunk, {h_q} rows")
 
 
+@pytest.mark.parametrize("h_q", [8, 16, 64, 128])
+def test_decode_fp8_large_scores_rescale(env, h_q):
+    """Every token's four group scales multiplied by 2^e, e rising from 0 to 4
+    along the cache (exact: powers of two), so that a row's scores grow by a few
+    hundred log2 units along its sequence and the running maximum moves several
+    times even under the split-wave kernel's 2^64 threshold: 16 rows
+    (token-split), 32, 128 and 256 rows (split-wave 64-row tiles) on FP8 pages."""
+    _, _, orc, fp8, _, _ = env
+    w = make_workload([3000, 640, 129], s_q=2, h_q=h_q, causal=True, seed=23)
+    kc8 = workloads.make_fp8_cache(w, seed=5)
+    n = w.num_pages * 64
+    e = (5 * np.arange(n) // n).astype(np.int32)  # 0 .. 4 over the token slots
+    rows = kc8.reshape(n, -1, kc8.shape[-1])
+    sc = rows[:, :, 512:528].copy().view(np.float32)
+    sc *= np.ldexp(np.float32(1.0), e)[:, None, None].astype(np.float32)
+    rows[:, :, 512:528] = sc.view(np.uint8)
+    go, gl = decode_fp8(env, w, kc8, num_parts=6)
+    ro, rl = orc.decode(dataclasses.replace(w, kcache=fp8.bf16_cache(kc8)))
+    assert np.nanmax(rl) - np.nanmin(rl[np.isfinite(rl)]) > 50  # the spread the test is for
+    check(go, gl, ro, rl, f"fp8 rescale, {w.rows} rows")
+
+
 @pytest.mark.parametrize("cfg", [2, 3, 4])
 def test_decode_fp8_64row_full_size(env, cfg):
     """compute_bound_full_heads (128 rows), spec_decode_causal (256 rows, causal)
