@@ -31,19 +31,16 @@
 //     units), so the O rescale is rare; the final normalisation uses the same
 //     reference max, which keeps the result exact up to rounding.
 //
-// Two kernels here (and the dispatch over all of them; the 64-row tiles of
-// paged pages are decode_qkpv.hip's, the 128-row tiles decode_wide.hip's):
+// This file holds the kernel for <= 16 query rows per KV head and the dispatch
+// over all decode kernels (64-row tiles: decode_qkpv.hip; 128-row tiles:
+// decode_wide.hip):
 //   decode_tokensplit  (<= 16 query rows per KV head, memory-bound shapes):
 //     each of the 4 waves owns 16 tokens of every page and an independent online
 //     softmax over them; the 4 states merge at the end of a chunk through LDS.
 //     It also runs on the FP8 cache (656-byte rows, see kF8RowBytes): pages
 //     stay FP8 in LDS and the MFMA operands are dequantised in registers, K
-//     with its per-group scale and V without, the V scale folded into P.
-//   decode_pairsplit  (64-row tiles of gathered rows: the token-sparse decode
-//     of more than 16 rows per KV head): QK^T is split 2 x 2 over rows and
-//     tokens (32 rows per wave, queries resident in registers), P goes through
-//     LDS, and PV is split by output dims (128 per wave), so each V element of
-//     a page is read from LDS once per workgroup.
+//     with its per-group scale and V without, the V scale folded into P, and
+//     on gathered rows (the token-sparse decode).
 #include <type_traits>
 #include <utility>
 
@@ -78,35 +75,6 @@ __device__ __forceinline__ void dma_slice_fp8(LDS_AS char* dst, i32x4_t rsrc, co
 #pragma unroll
   for (int k = 0; k < kF8SliceDma - 1; ++k) dma16(dst + 1024 * k, rsrc, d.off[k]);
   if (lane < kF8LastLanes) dma16(dst + 1024 * (kF8SliceDma - 1), rsrc, d.off[kF8SliceDma - 1]);
-}
-// Token-sparse decode.  A wave's 16-token slice of page blk of sequence b is
-// rows sp_offs[sp_rowptr[b] + 64 blk + 16 w + t], t < 16 (byte offsets; the
-// array is padded by one page, so a last page's reads stay inside it).  The 16
-// offsets move into LDS with one 16-lane transfer (4 bytes per lane), counted
-// with the page transfers, and each lane then reads the offsets of its two
-// tokens: no registers hold a page's offsets while it is in flight.
-__device__ __forceinline__ void dma4(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" MLA_DMA_TAIL
-               :
-               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)dst)), "v"(voffset), "s"(rsrc)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void stage_offs(LDS_AS char* dst, i32x4_t offs_rsrc, int row0, int blk, int w, int lane) {
-  if (lane < kSlice) dma4(dst, offs_rsrc, (row0 + blk * kPage + w * kSlice + lane) * 4);
-}
-// per-lane transfer offsets of a gathered slice: the swizzle of
-// slice_dma_offsets with each token's row read from the staged list; tokens past
-// the sequence's kept keys read zeros
-__device__ __forceinline__ SliceDma gathered_dma(const LDS_AS char* staged, int valid, int kvh, int lane) {
-  SliceDma d;
-#pragma unroll
-  for (int th = 0; th < 2; ++th) {
-    const int t = 8 * th + (lane >> 3);
-    uint32_t off = *(const LDS_AS uint32_t*)(staged + 4 * t);
-    if (t >= valid) off = kSparseNone;
-    d.vbase[th] = (int)(off + (uint32_t)(kvh * kRowBytes) + (uint32_t)(((lane & 7) ^ swz(t)) << 4));
-  }
-  return d;
 }
 
 
@@ -540,355 +508,6 @@ decode_tokensplit(DecodeParams p) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// 64-row tiles of gathered rows (token-sparse decode): pair-split kernel.
-// The 4 waves form a 2 x 2 grid: wave w owns query rows 32*(w&1) .. +31 (its
-// queries stay in registers) and tokens 32*(w>>1) .. +31 of every page for
-// QK^T.  The two waves of a row group agree on one running max per page through
-// LDS, so their P blocks share a reference; P goes to LDS and PV is split by
-// output dims (128 per wave, all 64 rows), which reads every V element of the
-// page from LDS once per workgroup.
-// LDS: two page buffers, P [64 rows x 64 tokens] bf16, the per-page row maxima
-// of both token groups, alpha, the end-of-chunk (m, l) of both token groups and
-// the gathered rows' byte offsets.  At a chunk end the page buffers stage each
-// wave's output rows.
-constexpr int kPsRows = 64;
-constexpr int kPsPbuf = 2 * kPageBytes;
-constexpr int kPsXmax = kPsPbuf + kPsRows * 128;
-constexpr int kPsAbuf = kPsXmax + 2 * kPsRows * 4;
-constexpr int kPsSbuf = kPsAbuf + kPsRows * 4;
-constexpr int kPsOffs = kPsSbuf + 2 * kPsRows * 2 * 4;  // token-sparse: [2 page slots][4 waves][16] row offsets
-// chunk end: per wave, its 128 output dims of the 64 rows as [row][dim] fp32
-// (row stride 132 floats) plus the rows' output offsets, inside the page buffers
-constexpr int kPsStgStride = 132;
-constexpr int kPsStgBytes = kPsRows * kPsStgStride * 4 + kPsRows * 8;
-static_assert(4 * kPsStgBytes <= kPsPbuf, "the chunk-end staging must fit in the page buffers");
-constexpr int kPsLds = kPsOffs + 2 * 4 * kSlice * 4;
-// transfer pieces of the next page issued during QK^T (the rest during PV)
-#ifndef MLA_QK_DMA
-#define MLA_QK_DMA 18
-#endif
-constexpr int kQkDma = MLA_QK_DMA;
-// transfer pieces issued during the softmax (after the QK^T ones); the rest go
-// during PV
-#ifndef MLA_SM_DMA
-#define MLA_SM_DMA 0
-#endif
-constexpr int kSmDma = MLA_SM_DMA;
-constexpr int kPvDma0 = kQkDma + kSmDma;
-
-// P row r holds 64 bf16 tokens as 8 chunks of 16 bytes; chunk c is stored at
-// position c ^ ((r >> 1) & 7), which keeps 16 consecutive rows reading the same
-// chunk on 16 different bank groups.
-__device__ __forceinline__ int pbuf_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
-
-__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
-decode_pairsplit(DecodeParams p) {
-  constexpr int kPg = kPageBytes;  // LDS bytes of one page
-  extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
-  LDS_AS char* smem = (LDS_AS char*)smem_generic;
-  LDS_AS char* pages = smem;
-  LDS_AS char* pbuf = smem + kPsPbuf;
-  LDS_AS float* xmax = (LDS_AS float*)(smem + kPsXmax);  // [2 token groups][64 rows]
-  LDS_AS float* abuf = (LDS_AS float*)(smem + kPsAbuf);  // [64 rows]
-  LDS_AS float* sbuf = (LDS_AS float*)(smem + kPsSbuf);  // [2 token groups][64 rows][2]
-
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int part, mt, kvh;
-  map_block(p, part, mt, kvh);
-  const int32_t* md = p.tile_md + (long long)part * kMdInts;
-  const int i0 = md[0], f0 = md[1], e0 = md[3], ord0 = md[4];
-  const int j0 = min(md[2], p.batch - 1);
-  if (i0 >= p.batch || i0 < 0) return;
-
-  const int l32 = lane & 31;
-  const int hb = lane >> 5;   // which 8-element half of a k-step this lane holds
-  const int g16 = lane >> 4;
-  const int k16 = lane & 15;
-  const int rg = w & 1;       // row group of this wave in QK
-  const int tg = w >> 1;      // token group of this wave in QK
-  const int trow = rg * 32 + l32;          // row inside the tile (QK phase)
-  const int qrow = mt * kPsRows + trow;
-  const bool qrow_ok = qrow < p.rows;
-
-  // K operand of QK: token 32*tg + l32 -> slice 2*tg + l32/16, token l32 & 15;
-  // chunk 2*ks + hb -> group ks/4, position 2*(ks&3) + hb.
-  int kaddr[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) kaddr[k] = (2 * tg + (l32 >> 4)) * kSliceBytes + slice_off(l32 & 15, 2 * k + hb);
-  // V^T operand of PV (transposed read) for tokens 16*ks + 8*(g16>>1) + k16/4 (+4):
-  // slice ks, token 8*(g16>>1) + k16/4 (+4); dims 128*w + 32*dt + 16*(g16&1) + 4*(k16&3)
-  // -> group 2*w + dt/2, position 4*(dt&1) + 2*(g16&1) + (k16&3)/2, byte 8*(k16&1).
-  int vaddr[2][2];
-#pragma unroll
-  for (int p4 = 0; p4 < 2; ++p4)
-#pragma unroll
-    for (int d1 = 0; d1 < 2; ++d1) {
-      const int t = 8 * (g16 >> 1) + (k16 >> 2) + 4 * p4;
-      const int pos = 4 * d1 + 2 * (g16 & 1) + ((k16 & 3) >> 1);
-      vaddr[p4][d1] = t * 128 + ((pos ^ swz(t)) << 4) + ((k16 & 1) << 3) + 2 * w * kGroupBytes;
-    }
-  // P^T operand of PV: row 32*rt + l32, tokens 16*ks + 8*hb .. +7 = chunk 2*ks + hb
-  int paddr[2][4];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) paddr[rt][ks] = pbuf_off(rt * 32 + l32, 2 * ks + hb);
-  const i32x4_t offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);  // the row-offset list
-
-  for (int b = i0; b <= j0; ++b) {
-    const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
-    int s;
-    long long qo;
-    row_coords(p, b, kvh, qrow_ok ? qrow : 0, s, qo);
-    const int nkeys = p.causal ? max(0, sr.L - p.s_q + s + 1) : sr.L;
-
-    // rows past the last one compute on row 0's query and are never stored
-    bf16x8_t qreg[36];
-    {
-      const bf16x8_t* qp = (const bf16x8_t*)(p.q + qo * kDqk);
-#pragma unroll
-      for (int ks = 0; ks < 36; ++ks) qreg[ks] = qp[2 * ks + hb];
-    }
-    f32x16_t O[4][2];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) O[dt][0] = O[dt][1] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.f;  // l_run covers this wave's token group only
-
-    // token-sparse: the sequence's rows are listed, not paged; the offsets of
-    // page blk + 1 are staged one page ahead (LDS slot by page parity)
-    const i32x4_t grsrc = make_rsrc(p.kcache, p.sp_cache_bytes);
-    const auto slice_valid = [&](int blk_) { return min(max(sr.L - blk_ * kPage - w * kSlice, 0), kSlice); };
-    LDS_AS char* offs_slot[2] = {smem + kPsOffs + w * 64, smem + kPsOffs + (4 + w) * 64};
-    const int row0 = ((const CONST_AS int32_t*)p.sp_rowptr)[b];
-    if (sr.lo < sr.hi) {
-      stage_offs(offs_slot[0], offs_rsrc, row0, sr.lo, w, lane);
-      if (sr.lo + 1 < sr.hi) stage_offs(offs_slot[1], offs_rsrc, row0, sr.lo + 1, w, lane);
-      wait_vmcnt<0>();
-      dma_slice(pages + w * kSliceBytes, grsrc, gathered_dma(offs_slot[0], slice_valid(sr.lo), kvh, lane));
-    }
-    for (int blk = sr.lo; blk < sr.hi; ++blk) {
-      const int pb = (blk - sr.lo) & 1;
-      wait_vmcnt<0>();
-      wg_barrier();  // page blk visible; the other buffer, P and xmax are free
-      // the next page's slice moves in pieces spread over this page's MFMAs:
-      // kQkDma pieces during QK^T, the rest during PV
-      const bool has_next = blk + 1 < sr.hi;
-      LDS_AS char* npage = pages + (pb ^ 1) * kPg;
-      LDS_AS char* ndst = npage + w * kSliceBytes;
-      i32x4_t nrsrc = {0, 0, 0, 0};
-      SliceDma ndma = {};
-      if (has_next) {
-        const int ns = (blk + 1 - sr.lo) & 1;
-        nrsrc = grsrc;
-        ndma = gathered_dma(offs_slot[ns], slice_valid(blk + 1), kvh, lane);
-        if (blk + 2 < sr.hi) stage_offs(offs_slot[ns ^ 1], offs_rsrc, row0, blk + 2, w, lane);
-      }
-      const LDS_AS char* page = pages + pb * kPg;
-
-      // ---- S^T[32 tokens x 32 rows] = K . Q^T, two accumulation chains,
-      // K operands fetched kAhead k-steps ahead.  The loop is instantiated with
-      // and without the next page's transfer pieces so that no branch splits it.
-      auto qk = [&](auto with_dma) {
-        f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
-        constexpr int kAhead = 4;  // K operands in flight ahead of the MFMA that uses them
-        bf16x8_t ka[kAhead + 1];
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i)
-          ka[i] = *(const LDS_AS bf16x8_t*)(page + kaddr[i & 3] + (i >> 2) * kGroupBytes);
-        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-          if (ks + kAhead < 36) {
-            const int n = ks + kAhead;
-            ka[n % (kAhead + 1)] = *(const LDS_AS bf16x8_t*)(page + kaddr[n & 3] + (n >> 2) * kGroupBytes);
-          }
-          if (ks & 1) S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S1, 0, 0, 0);
-          else S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks % (kAhead + 1)], qreg[ks], S0, 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (ks + kAhead < 36) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if constexpr (decltype(with_dma)::value) {
-#pragma unroll
-            for (int i = ks * kQkDma / 36; i < (ks + 1) * kQkDma / 36; ++i) dma_piece(ndst, nrsrc, ndma, i);
-          }
-        }
-        return S0 + S1;
-      };
-      f32x16_t S;
-      if (has_next) S = qk(std::true_type{});
-      else S = qk(std::false_type{});
-      __builtin_amdgcn_sched_barrier(0);
-      // lane holds row trow, tokens 32*tg + 8*(r>>2) + 4*hb + (r&3) of the page.
-      // Scores stay unscaled (the scale is positive, so the max commutes with
-      // it) and keys past a row's last visible one are masked only on a page
-      // that some row of the wave does not see whole.
-      const int tok0 = blk * kPage + 32 * tg + 4 * hb;
-      if (__builtin_amdgcn_ballot_w64((blk + 1) * kPage > nkeys)) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (tok0 + 8 * (r >> 2) + (r & 3) >= nkeys) S[r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
-      mx = half_max(mx) * p.scale_log2;
-      if (hb == 0) xmax[tg * kPsRows + trow] = mx;
-      wg_barrier();  // both token groups' maxima visible
-      mx = fmaxf(mx, xmax[(tg ^ 1) * kPsRows + trow]);
-      float alpha = 1.f;
-      if (mx > m_run + kTau) {  // identical decision in both waves of the row group
-        alpha = __builtin_amdgcn_exp2f(m_run - mx);
-        m_run = mx;
-        l_run *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        S[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, -m_use));
-        ps += S[r];
-        if (kSmDma > 0 && has_next && r % 4 == 3) {
-          for (int i = kQkDma + (r / 4) * kSmDma / 4; i < kQkDma + (r / 4 + 1) * kSmDma / 4; ++i)
-            dma_piece(ndst, nrsrc, ndma, i);
-        }
-      }
-      l_run += half_sum(ps);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2_t v = {pack_bf16(S[4 * j], S[4 * j + 1]), pack_bf16(S[4 * j + 2], S[4 * j + 3])};
-        *(LDS_AS u32x2_t*)(pbuf + pbuf_off(trow, 4 * tg + j) + hb * 8) = v;
-      }
-      if (tg == 0 && hb == 0) abuf[trow] = alpha;
-      __builtin_amdgcn_sched_barrier(0);
-      wg_barrier();  // P and alpha visible
-
-      // ---- O^T[128 dims x 64 rows] += V^T . P^T over the page's 64 tokens
-      {
-        const float a0 = abuf[l32], a1 = abuf[32 + l32];
-        if (__builtin_amdgcn_ballot_w64(a0 != 1.f || a1 != 1.f)) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            O[dt][0] *= a0;
-            O[dt][1] *= a1;
-          }
-        }
-      }
-      // operands of k-step ks (16 tokens): P^T for both row tiles and V^T for the
-      // four 32-dim tiles; the next k-step's operands load while this one's
-      // MFMAs run
-      struct PvOps {
-        bf16x8_t bp[2];
-        bf16x8_t va[4];
-      };
-      auto load_ops = [&](int ks) {
-        PvOps o;
-        o.bp[0] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[0][ks]);
-        o.bp[1] = *(const LDS_AS bf16x8_t*)(pbuf + paddr[1][ks]);
-        const LDS_AS char* vs = page + ks * kSliceBytes;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int go = (dt >> 1) * kGroupBytes;
-          const bf16x4_t v0 = lds_tr16(vs + vaddr[0][dt & 1] + go);
-          const bf16x4_t v1 = lds_tr16(vs + vaddr[1][dt & 1] + go);
-          o.va[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        return o;
-      };
-      PvOps ops[2];
-      ops[0] = load_ops(0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
-          ops[(ks + 1) & 1] = load_ops(ks + 1);
-        }
-        const PvOps& o = ops[ks & 1];
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          O[dt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[0], O[dt][0], 0, 0, 0);
-          O[dt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.va[dt], o.bp[1], O[dt][1], 0, 0, 0);
-        }
-        if (has_next) {
-          for (int i = kPvDma0 + ks * (kSliceDma - kPvDma0) / 4; i < kPvDma0 + (ks + 1) * (kSliceDma - kPvDma0) / 4;
-               ++i)
-            dma_piece(ndst, nrsrc, ndma, i);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- epilogue: (m, l) of both token groups for every row
-    if (hb == 0) {
-      sbuf[(tg * kPsRows + trow) * 2 + 0] = m_run;
-      sbuf[(tg * kPsRows + trow) * 2 + 1] = l_run;
-    }
-    wg_barrier();  // ... and every wave is done with the page buffers
-    const bool split = sr.chunks > 1;
-    const long long slot = (long long)(sr.base + sr.ord) * p.h_kv + kvh;
-    // Each wave writes its 128 normalised output dims of the 64 rows into its
-    // own region of the page buffers as [row][dim], with every row's output
-    // offset (elements; -1 for a row that is not stored), and then stores whole
-    // row segments: 512 B of fp32 partial per 32 lanes or 256 B of bf16 output
-    // per 16 lanes, instead of 16-byte pieces spread over 32 rows.
-    LDS_AS float* stg = (LDS_AS float*)(smem + w * kPsStgBytes);
-    LDS_AS long long* roff = (LDS_AS long long*)(smem + w * kPsStgBytes + kPsRows * kPsStgStride * 4);
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int rl = rt * 32 + l32;
-      const int orow = mt * kPsRows + rl;
-      const float mrow = sbuf[rl * 2 + 0];  // same reference in both token groups
-      const float lrow = sbuf[rl * 2 + 1] + sbuf[(kPsRows + rl) * 2 + 1];
-      const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4_t v = {O[dt][rt][4 * j], O[dt][rt][4 * j + 1], O[dt][rt][4 * j + 2], O[dt][rt][4 * j + 3]};
-          *(LDS_AS f32x4_t*)(stg + rl * kPsStgStride + dt * 32 + 8 * j + 4 * hb) = v * inv;
-        }
-      if (hb == 0) {
-        long long off = -1;
-        if (orow < p.rows && sr.ok) {
-          int os;
-          long long oo;
-          row_coords(p, b, kvh, orow, os, oo);
-          const long long srow = slot * p.rows + orow;
-          off = (split ? srow : oo) * kDv;
-          if (w == 0) {
-            const float l2 = lrow > 0.f ? mrow + __builtin_amdgcn_logf(lrow) : -INFINITY;
-            if (split) p.lse_acc[srow] = l2;
-            else p.lse[oo] = l2 * kLn2;
-          }
-        }
-        roff[rl] = off;
-      }
-    }
-    // this wave's own LDS writes are visible to its later reads (in order)
-    if (split) {
-#pragma unroll 8
-      for (int i = 0; i < kPsRows / 2; ++i) {
-        const int r = 2 * i + (lane >> 5);
-        const long long off = roff[r];
-        const f32x4_t v = *(const LDS_AS f32x4_t*)(stg + r * kPsStgStride + 4 * (lane & 31));
-        if (off >= 0) *(f32x4_t*)(p.o_acc + off + w * 128 + 4 * (lane & 31)) = v;
-      }
-    } else {
-#pragma unroll 8
-      for (int i = 0; i < kPsRows / 4; ++i) {
-        const int r = 4 * i + (lane >> 4);
-        const long long off = roff[r];
-        const LDS_AS float* src = stg + r * kPsStgStride + 8 * (lane & 15);
-        const f32x4_t v0 = *(const LDS_AS f32x4_t*)src;
-        const f32x4_t v1 = *(const LDS_AS f32x4_t*)(src + 4);
-        const u32x4_t pk = {pack_bf16(v0[0], v0[1]), pack_bf16(v0[2], v0[3]), pack_bf16(v1[0], v1[1]),
-                            pack_bf16(v1[2], v1[3])};
-        if (off >= 0) *(u32x4_t*)(p.out + off + w * 128 + 8 * (lane & 15)) = pk;
-      }
-    }
-    wg_barrier();  // sbuf and page buffers are reused by the next sequence
-  }
-}
-
 template <auto Kernel>
 hipError_t launch_one(int lds, const DecodeParams& p, hipStream_t stream) {
   // allow the kernel more than the default 64 KB of dynamic LDS (once per
@@ -910,12 +529,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     return launch_one<decode_tokensplit<false>>(TsLayout<false>::kLds, p, stream);
   }
   if (tile_rows_for(p.rows) == 128 && !p.kv_fp8 && !p.sparse) return launch_decode_wide(p, stream);
-  // 64-row tiles (any row count on FP8 pages and gathered rows): the pair-split
-  // kernel for gathered rows, the split-wave kernel for pages
+  // 64-row tiles (any row count on FP8 pages and gathered rows): the split-wave
+  // kernel
   DecodeParams q = p;
-  q.m_tiles = pair_tiles_for(p.rows);
+  q.m_tiles = tiles64_for(p.rows);
   q.xcd_map = (q.m_tiles * q.h_kv > 1 && q.num_parts % 8 == 0) ? 1 : 0;
-  if (q.sparse) return launch_one<decode_pairsplit>(kPsLds, q, stream);
   return launch_decode_qkpv(q, stream);
 }
 

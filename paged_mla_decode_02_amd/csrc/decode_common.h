@@ -249,6 +249,36 @@ __device__ __forceinline__ void dma16(LDS_AS char* dst, i32x4_t rsrc, int voffse
                : "s"((unsigned)(size_t)dst), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
+// Token-sparse decode.  A wave's 16-token slice of page blk of sequence b is
+// rows sp_offs[sp_rowptr[b] + 64 blk + 16 w + t], t < 16 (byte offsets; the
+// array is padded by one page, so a last page's reads stay inside it).  The 16
+// offsets move into LDS with one 16-lane transfer (4 bytes per lane), counted
+// with the page transfers, and each lane then reads the offsets of its two
+// tokens: no registers hold a page's offsets while it is in flight.
+__device__ __forceinline__ void dma4(LDS_AS char* dst, i32x4_t rsrc, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" MLA_DMA_TAIL
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)dst)), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void stage_offs(LDS_AS char* dst, i32x4_t offs_rsrc, int row0, int blk, int w, int lane) {
+  if (lane < kSlice) dma4(dst, offs_rsrc, (row0 + blk * kPage + w * kSlice + lane) * 4);
+}
+// per-lane transfer offsets of a gathered slice: the swizzle of
+// slice_dma_offsets with each token's row read from the staged list; tokens past
+// the sequence's kept keys read zeros
+__device__ __forceinline__ SliceDma gathered_dma(const LDS_AS char* staged, int valid, int kvh, int lane) {
+  SliceDma d;
+#pragma unroll
+  for (int th = 0; th < 2; ++th) {
+    const int t = 8 * th + (lane >> 3);
+    uint32_t off = *(const LDS_AS uint32_t*)(staged + 4 * t);
+    if (t >= valid) off = kSparseNone;
+    d.vbase[th] = (int)(off + (uint32_t)(kvh * kRowBytes) + (uint32_t)(((lane & 7) ^ swz(t)) << 4));
+  }
+  return d;
+}
+
 template <int G>
 __device__ __forceinline__ void dma_group(LDS_AS char* dst, i32x4_t rsrc, const SliceDma& d) {
   dma16(dst + G * kGroupBytes, rsrc, d.vbase[0] + G * 128);

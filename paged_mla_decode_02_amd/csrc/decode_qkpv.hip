@@ -38,6 +38,12 @@
 // value waves read V^T with the 8-bit transposed read and convert it without
 // scale, and fold each token's scale for the 128-dim group of an MFMA into the
 // P^T entries that multiply it (every scale is a power of two: exact).
+//
+// Gathered rows (the token-sparse decode, decode_qkpv<false, true>): a slice
+// of half page h is the 16 cache rows whose byte offsets the caller lists for
+// it; a value wave brings its slice's 16 offsets into LDS (one 16-lane
+// transfer) a step before it requests the rows, in the same order as the
+// slices, so the step's transfer wait covers them too.
 #include "decode_common.h"
 
 namespace mla {
@@ -93,6 +99,9 @@ struct QLay {
   static constexpr int kLbuf = kSbuf + (kFp8 ? 2 * 4 * kQHalf * 4 : 0);
   static constexpr int kRbuf = kLbuf + kQRows * 4;
   static constexpr int kLds = kRbuf + kQRows * 4;
+  // gathered rows: 2 value waves x 2 half pages x 16 staged row offsets
+  static constexpr int kObuf = kLds;
+  static constexpr int kSparseLds = kObuf + 2 * 2 * kSlice * 4;
   // transfers per value wave wk per half page: 18 (bf16); FP8 transfers wk,
   // wk + 2, .. of the 21
   static constexpr int dmas(int wk) { return kFp8 ? (kQF8Dma + 1 - wk) / 2 : kQDma; }
@@ -109,9 +118,10 @@ __host__ __device__ constexpr int dma_at(int i) {
   return -1;
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kSparse>
 __global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 decode_qkpv(DecodeParams p) {
+  static_assert(!(kFp8 && kSparse), "the token-sparse decode reads bf16 rows");
   using L = QLay<kFp8>;
   extern __shared__ __attribute__((aligned(1024))) char smem_generic[];
   LDS_AS char* smem = (LDS_AS char*)smem_generic;
@@ -184,6 +194,13 @@ decode_qkpv(DecodeParams p) {
     }
     f8half = kQHalf * p.h_kv * kF8RowBytes;
   }
+  // gathered rows: the offset list and the cache as buffer resources (offsets
+  // past the cache, kSparseNone included, read zeros)
+  i32x4_t offs_rsrc = {}, grsrc = {};
+  if constexpr (kSparse) {
+    offs_rsrc = make_rsrc(p.sp_offs, 0xffffffffu);
+    grsrc = make_rsrc(p.kcache, p.sp_cache_bytes);
+  }
 
   for (int b = i0; b <= j0; ++b) {
     const SeqRange sr = seq_range(p, b, i0, f0, j0, e0, ord0);
@@ -197,10 +214,25 @@ decode_qkpv(DecodeParams p) {
     // One page loop per kind of wave (the same barriers, step for step), so
     // that the score waves' queries and the value waves' O are never live in
     // the same code.
-    int ids = load_page_ids(p, b, sr.lo, lane);
+    int ids = kSparse ? 0 : load_page_ids(p, b, sr.lo, lane);
     auto half_rsrc = [&](int h) {
       const int blk = h >> 1;
       return page_rsrc(p, page_id(ids, (blk - sr.lo) & 63), blk, sr.L, kFp8 ? kF8RowBytes : kRowBytes);
+    };
+    // gathered rows: row0 indexes the sequence's offset list; gd holds the
+    // per-lane sources of the slice being requested
+    const int row0 = kSparse ? ((const CONST_AS int32_t*)p.sp_rowptr)[b] : 0;
+    SliceDma gd = {};
+    LDS_AS char* const obuf = smem + L::kObuf + 2 * wk * kSlice * 4;
+    // offsets of slice wk of half page hd into its staging slot (hd % 2): none
+    // past the chunk's end, so the list is never read beyond it
+    auto stage_half = [&](int hd) {
+      if (hd < h1) stage_offs(obuf + (hd & 1) * kSlice * 4, offs_rsrc, row0 + kQHalf * hd, 0, wk, lane);
+    };
+    // the slice's sources from its staged offsets; keys past the sequence read zeros
+    auto gather_half = [&](int hd) {
+      const int valid = hd < h1 ? min(max(sr.L - kQHalf * hd - kSlice * wk, 0), kSlice) : 0;
+      return gathered_dma(obuf + (hd & 1) * kSlice * 4, valid, kvh, lane);
     };
     // transfer i (0..17) of half page h by a value wave: chunk group i / 2
     // (group 8 is the rope part), token half i % 2
@@ -215,13 +247,29 @@ decode_qkpv(DecodeParams p) {
         (void)rope;
       } else {
         const int g = i >> 1, th = i & 1;
-        const int vb = ((h & 1) ? (th ? d1.vbase[1] : d1.vbase[0]) : (th ? d0.vbase[1] : d0.vbase[0])) + g * 128;
+        const int vb = kSparse ? gd.vbase[th] + g * 128
+                               : ((h & 1) ? (th ? d1.vbase[1] : d1.vbase[0]) : (th ? d0.vbase[1] : d0.vbase[0])) + g * 128;
         if (g < 8) dma16(smem + kQLat + lat * kQLatSlot + wk * kQLatSlice + g * kGroupBytes + th * 1024, r, vb);
         else dma16(smem + kQRope + rope * kQRopeSlot + wk * kGroupBytes + th * 1024, r, vb);
       }
     };
     constexpr int kMaxDma = kFp8 ? kF8Mine : kQDma;
     auto prologue_dma = [&]() {
+      if constexpr (kSparse) {
+        // offsets of h0 and h0 + 1, then their rows; h0 + 2's offsets go into
+        // h0's staging slot once h0's have been read, before h0 + 1's rows
+        stage_half(h0);
+        stage_half(h0 + 1);
+        wait_vmcnt<0>();
+        gd = gather_half(h0);
+#pragma unroll
+        for (int g = 0; g < kQDma; ++g) dma_piece_h(h0, grsrc, 0, 0, g);
+        stage_half(h0 + 2);
+        gd = gather_half(h0 + 1);
+#pragma unroll
+        for (int g = 0; g < kQDma; ++g) dma_piece_h(h0 + 1, grsrc, 1, 1, g);
+        return;
+      }
 #pragma unroll
       for (int k = 0; k < L::kSlots - 2; ++k) {
         const i32x4_t r = h0 + k < h1 ? half_rsrc(h0 + k) : make_rsrc(p.kcache, 0u);
@@ -550,7 +598,15 @@ decode_qkpv(DecodeParams p) {
         }
         wg_barrier();
         const int hd = h + L::kSlots - 1;
-        const i32x4_t dr = step_rsrc(hd);
+        i32x4_t dr;
+        if constexpr (kSparse) {
+          // h + 3's offsets landed with the wait above; h + 4's go into h + 2's slot
+          gd = gather_half(hd);
+          stage_half(hd + 1);
+          dr = grsrc;
+        } else {
+          dr = step_rsrc(hd);
+        }
         auto between = [&](int i) {
           const int g = dma_at<kMaxDma>(i);
           if (g >= 0 && (!kFp8 || g < L::dmas(wk))) dma_piece_h(hd, dr, latd, rope, g);
@@ -626,21 +682,23 @@ decode_qkpv(DecodeParams p) {
   wait_vmcnt<0>();
 }
 
-template <bool kFp8>
+template <bool kFp8, bool kSparse>
 hipError_t launch_qkpv(const DecodeParams& p, hipStream_t stream) {
-  constexpr int lds = QLay<kFp8>::kLds;
+  constexpr int lds = kSparse ? QLay<kFp8>::kSparseLds : QLay<kFp8>::kLds;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)decode_qkpv<kFp8>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      hipFuncSetAttribute((const void*)decode_qkpv<kFp8, kSparse>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const int grid = p.num_parts * p.m_tiles * p.h_kv;
-  hipLaunchKernelGGL(decode_qkpv<kFp8>, dim3(grid), dim3(kThreads), lds, stream, p);
+  hipLaunchKernelGGL((decode_qkpv<kFp8, kSparse>), dim3(grid), dim3(kThreads), lds, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode_qkpv(const DecodeParams& p, hipStream_t stream) {
-  return p.kv_fp8 ? launch_qkpv<true>(p, stream) : launch_qkpv<false>(p, stream);
+  if (p.sparse) return launch_qkpv<false, true>(p, stream);
+  return p.kv_fp8 ? launch_qkpv<true, false>(p, stream) : launch_qkpv<false, false>(p, stream);
 }
 
 }  // namespace mla

@@ -27,9 +27,9 @@ constexpr int kF8RowBytes = kLatent + 4 * (kLatent / kF8Group) + 2 * kRope;
 // more the 128-row kernel (ceil(rows / 128) row tiles).  At 128 rows the
 // 128-row kernel would need twice the parts to fill the GPU, and the extra
 // split partials cost more than its faster tile saves.  The FP8 and
-// token-sparse decodes keep 64-row tiles for any row count (pair_tiles_for).
+// token-sparse decodes keep 64-row tiles for any row count (tiles64_for).
 __host__ __device__ constexpr int tile_rows_for(int rows) { return rows <= 16 ? 16 : rows <= 128 ? 64 : 128; }
-__host__ __device__ constexpr int pair_tiles_for(int rows) { return (rows + 63) / 64; }
+__host__ __device__ constexpr int tiles64_for(int rows) { return (rows + 63) / 64; }
 // Fixed per-chunk cost, in page units, that the scheduler charges before each
 // sequence: loading the query tile, the end-of-chunk merge and writing /
 // re-reading a split partial.  The 16-row token-split kernel's chunk end (a merge

@@ -6,7 +6,7 @@ not visible to the compiler); a miscounted wait would let a wave read a page
 slot before its bytes land, which is a timing-dependent race that can pass a
 parity check by luck.  Here the arithmetic is identical, so out and lse must be
 bit-identical on every case: every decode kernel (16-row token-split, 64-row
-split-wave, 64-row pair-split for gathered rows, 128-row), bf16 and FP8 pages,
+split-wave on pages and gathered rows, 128-row), bf16 and FP8 pages,
 the token-sparse gather, forced splits, ragged tiles and chunks longer than 64 pages.  Each
 pipelined result is also computed twice (run-to-run determinism)."""
 
