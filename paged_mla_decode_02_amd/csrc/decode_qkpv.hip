@@ -1,7 +1,8 @@
 // Paged MLA decode, 64-row tiles with two kinds of waves: the kernel for 17 to
 // 64 query rows per KV head, and for each 64-row tile of more rows (65 to 128
-// on bf16 pages, any number on FP8 pages).  Same method as decode.hip and decode_wide.hip -- every latent page
-// read from HBM is multiplied against all query rows that share its KV head
+// on bf16 pages; any number on FP8 pages and gathered rows).  Same method as
+// decode.hip and decode_wide.hip -- every latent page read from HBM is
+// multiplied against all query rows that share its KV head
 // ("OpenSourceWeek Day 1 -- Demystifying DeepSeek's FlashMLA",
 // deepseekonline.chat, §II.1), the softmax is computed online with a running
 // max and sum and equals the textbook result ("FlashMLA inference
@@ -71,11 +72,10 @@ static_assert(kQLds <= 160 * 1024, "LDS budget");
 // 2^8 (the other kernels' threshold) a workload whose keys include 1 % scaled
 // outliers rescaled about a fifth of its steps.  P then stays below 2^64 and
 // the sums below 2^64 times the key count: far inside the bf16 / fp32
-// exponent range (bf16 pages only: no FP8 scale multiplies P here).
+// exponent range.  On FP8 pages P^T is multiplied by power-of-two group scales
+// before PV; those products stay finite while 2^64 times the values of V does,
+// which the fp32 sums of O need on either kind of page.
 constexpr float kQTau = 64.0f;
-// (On FP8 pages P^T is multiplied by power-of-two group scales before PV: the
-// products stay finite while 2^64 times the values of V does, which the fp32
-// sums of O need on either kind of page.)
 
 // FP8 pages: four slots of 32 token-major 656-byte rows, inside the 128 KB the
 // chunk-end staging takes; P, alpha, the group-scale tables, 1 / l and the row
