@@ -25,6 +25,7 @@ constexpr int kThreadsPerRow = kDv / 4;  // 4 dims per thread, two waves per row
 constexpr int kTile = 256;               // chunk weights staged in LDS at a time
 constexpr int kUnroll = 8;               // partial loads in flight per thread
 constexpr int kFew = 8;                  // up to this many chunks: single-pass path
+constexpr int kPre = 4;                  // partials loaded with the lse values (more chunks)
 static_assert(kFew == 8, "combine_few is instantiated for 2..8 chunks");
 struct LDS_float_pair {
   float v[2];
@@ -120,16 +121,38 @@ __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel
     return;
   }
 
+  // The first kPre partials do not depend on the weights: their loads go out
+  // together with the lse loads, so the two round trips overlap.
+  const long long cstride = stride * kDv;  // floats between consecutive chunks' partials
+  f32x4_t v0[kPre];
+  if (row_ok) {
+    const float* src = p.o_acc + r0 * kDv + d0;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) v0[u] = *(const f32x4_t*)(src + u * cstride);  // nsp > kFew > kPre
+  }
+  // With at most one chunk per thread (nsp <= kThreadsPerRow) each lse is read
+  // once and kept for the sum and the weights.
+  const bool one = nsp <= kThreadsPerRow;
+  float lt = -INFINITY;
   float M = -INFINITY;
   if (row_ok)
-    for (int s = t; s < nsp; s += kThreadsPerRow) M = fmaxf(M, p.lse_acc[r0 + s * stride]);
-  M = row_reduce(M, true, red, rl, wv);
-  float wsum = 0.f;
-  if (row_ok && M != -INFINITY)
     for (int s = t; s < nsp; s += kThreadsPerRow) {
       const float l = p.lse_acc[r0 + s * stride];
-      wsum += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M);
+      if (s == t) lt = l;
+      M = fmaxf(M, l);
     }
+  M = row_reduce(M, true, red, rl, wv);
+  float wsum = 0.f;
+  if (row_ok && M != -INFINITY) {
+    if (one) {
+      wsum = (lt == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(lt - M);
+    } else {
+      for (int s = t; s < nsp; s += kThreadsPerRow) {
+        const float l = p.lse_acc[r0 + s * stride];
+        wsum += (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M);
+      }
+    }
+  }
   wsum = row_reduce(wsum, false, red, rl, wv);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 
@@ -139,7 +162,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel
     for (int j = t; j < kTile; j += kThreadsPerRow) {
       float wgt = 0.f;
       if (row_ok && j < n && M != -INFINITY) {
-        const float l = p.lse_acc[r0 + (s0 + j) * stride];
+        const float l = one ? lt : p.lse_acc[r0 + (s0 + j) * stride];  // one: s0 = 0 and j = t
         wgt = (l == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(l - M) * inv;
       }
       wts[rl][j] = wgt;
@@ -147,12 +170,18 @@ __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel
     __syncthreads();
     if (row_ok) {
       const float* src = p.o_acc + (r0 + s0 * stride) * kDv + d0;
-      for (int j0 = 0; j0 < n; j0 += kUnroll) {
+      int jb = 0;
+      if (s0 == 0) {  // the first kPre chunks, already loaded (n > kPre)
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) acc += wts[rl][u] * v0[u];
+        jb = kPre;
+      }
+      for (int j0 = jb; j0 < n; j0 += kUnroll) {
         f32x4_t v[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           const int j = min(j0 + u, n - 1);  // past the end: weight 0, any valid slot
-          v[u] = *(const f32x4_t*)(src + j * stride * kDv);
+          v[u] = *(const f32x4_t*)(src + j * cstride);
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) acc += wts[rl][min(j0 + u, kTile - 1)] * (j0 + u < n ? v[u] : f32x4_t{});
