@@ -20,7 +20,9 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kRowsPerBlock = 2;
+// one row per workgroup: twice the workgroups of two rows, so a CU holds more
+// partial loads in flight on rows with many chunks
+constexpr int kRowsPerBlock = 1;
 constexpr int kThreadsPerRow = kDv / 4;  // 4 dims per thread, two waves per row
 constexpr int kTile = 256;               // chunk weights staged in LDS at a time
 constexpr int kUnroll = 8;               // partial loads in flight per thread
