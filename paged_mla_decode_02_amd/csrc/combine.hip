@@ -20,14 +20,10 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-// one row per workgroup: twice the workgroups of two rows, so a CU holds more
-// partial loads in flight on rows with many chunks
-constexpr int kRowsPerBlock = 1;
 constexpr int kThreadsPerRow = kDv / 4;  // 4 dims per thread, two waves per row
 constexpr int kTile = 256;               // chunk weights staged in LDS at a time
 constexpr int kUnroll = 8;               // partial loads in flight per thread
 constexpr int kFew = 8;                  // up to this many chunks: single-pass path
-constexpr int kPre = 4;                  // partials loaded with the lse values (more chunks)
 static_assert(kFew == 8, "combine_few is instantiated for 2..8 chunks");
 struct LDS_float_pair {
   float v[2];
@@ -83,13 +79,14 @@ __device__ __forceinline__ float row_reduce(float v, bool is_max, LDS_float_pair
   return r;
 }
 
-// One workgroup merges kRowsPerBlock rows of one (sequence, KV head): each row's
+// One workgroup merges R rows of one (sequence, KV head): each row's
 // 128 threads first reduce max_s l_s and sum_s 2^(l_s - M) over the chunks, then
 // normalised chunk weights go through LDS kTile at a time and every thread
 // accumulates its 4 dims over the chunks with kUnroll loads in flight.
-__global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel(DecodeParams p) {
-  __shared__ float wts[kRowsPerBlock][kTile];
-  __shared__ LDS_float_pair red[kRowsPerBlock];
+template <int R>
+__global__ __launch_bounds__(R * kThreadsPerRow) void combine_kernel(DecodeParams p) {
+  __shared__ float wts[R][kTile];
+  __shared__ LDS_float_pair red[R];
   const int b = blockIdx.x;
   const int kvh = blockIdx.z;
   const int base = p.num_splits[b];
@@ -99,7 +96,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel
   const int rl = threadIdx.x / kThreadsPerRow;
   const int t = threadIdx.x % kThreadsPerRow;
   const int wv = t / 64;
-  const int row = blockIdx.y * kRowsPerBlock + rl;
+  const int row = blockIdx.y * R + rl;
   const bool row_ok = row < p.rows;  // uniform over the row's two waves
   const int d0 = t * 4;
 
@@ -124,9 +121,12 @@ __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel
   }
 
   // The first kPre partials do not depend on the weights: their loads go out
-  // together with the lse loads, so the two round trips overlap.
+  // together with the lse loads, so the two round trips overlap.  Only in the
+  // one-row form, which serves rows with many chunks: the registers they take
+  // would cost the two-row form a wave per SIMD.
+  constexpr int kPre = R == 1 ? 4 : 0;
   const long long cstride = stride * kDv;  // floats between consecutive chunks' partials
-  f32x4_t v0[kPre];
+  f32x4_t v0[kPre > 0 ? kPre : 1];
   if (row_ok) {
     const float* src = p.o_acc + r0 * kDv + d0;
 #pragma unroll
@@ -200,8 +200,18 @@ __global__ __launch_bounds__(kRowsPerBlock * kThreadsPerRow) void combine_kernel
 }  // namespace
 
 hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.batch, (p.rows + kRowsPerBlock - 1) / kRowsPerBlock, p.h_kv);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kRowsPerBlock * kThreadsPerRow), 0, stream, p);
+  // Rows per workgroup.  When sequences average more than 8 chunks (more parts
+  // than 8 per sequence), rows take the many-chunk path, which is bound by the
+  // partial loads a CU keeps in flight: one row per workgroup doubles the
+  // workgroups, and so the loads in flight.  With few chunks per row, two rows
+  // per workgroup halve the workgroups to launch, which costs less.
+  if (p.num_parts > 8 * p.batch) {
+    dim3 grid(p.batch, p.rows, p.h_kv);
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kThreadsPerRow), 0, stream, p);
+  } else {
+    dim3 grid(p.batch, (p.rows + 1) / 2, p.h_kv);
+    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(2 * kThreadsPerRow), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
