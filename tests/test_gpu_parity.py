@@ -210,6 +210,10 @@ EDGE = [
     ([1200, 5], 2, 100, 1, True, None),                # 200 rows
     ([4100], 1, 129, 1, False, 32),                    # 129 rows: a one-row second tile, many splits
     ([300, 2000], 5, 64, 2, True, 6),                  # two KV heads of 160 rows
+    # the combine's two-row form (num_parts <= 8 * batch) on rows with more
+    # than 8 chunks: 24 chunks, and 313 (lse values re-read, two weight tiles)
+    ([9000, 100, 100, 100], 1, 16, 1, False, 32),
+    ([120000] + [64] * 63, 1, 16, 1, False, 500),
 ]
 
 
