@@ -205,7 +205,7 @@ hipError_t launch_combine(const DecodeParams& p, hipStream_t stream) {
   // partial loads a CU keeps in flight: one row per workgroup doubles the
   // workgroups, and so the loads in flight.  With few chunks per row, two rows
   // per workgroup halve the workgroups to launch, which costs less.
-  if (p.num_parts > 8 * p.batch) {
+  if ((long long)p.num_parts > 8LL * p.batch) {
     dim3 grid(p.batch, p.rows, p.h_kv);
     hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kThreadsPerRow), 0, stream, p);
   } else {
